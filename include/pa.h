@@ -1,0 +1,149 @@
+/*
+ * pa.h — C ABI of the paged KV-cache attention library (MI355X / gfx950).
+ *
+ * Sources cited below:
+ *   P1 = "Efficient Memory Management for Large Language Model Serving with
+ *         PagedAttention" (paper review, urban-dandelion.tistory.com/4)
+ *   P2 = "SOSP 2023論文解説: vLLM — PagedAttentionによるKVキャッシュメモリ管理の革新"
+ *         (0h-n0.github.io/posts/conf-vllm-pagedattention)
+ *   P3 = "연속 배치 처리 아키텍처" (Transformers docs, continuous batching architecture)
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer except the names given as host values is DEVICE memory,
+ *     owned by the caller; the library keeps no pointer after returning, keeps
+ *     no state between calls and allocates nothing.  Calls are thread-safe.
+ *   - Tensors are dense, row-major, contiguous.
+ *   - K/V pools: k_pool and v_pool, each [num_blocks][block_size][num_heads][head_dim]
+ *     elements of `dtype`: one physical block holds block_size token rows, a
+ *     token row holds every head's head_dim vector (the per-block
+ *     (block_size, num_heads, head_dim) tensor of P2, pseudocode section).
+ *     Byte offsets are computed in 64 bits; pools may exceed 2^31 bytes.
+ *   - block_tables: int32 [num_seqs][max_blocks_per_seq]; entry b of row s is
+ *     the physical block holding tokens b*block_size .. b*block_size+block_size-1
+ *     of sequence s (P1 sec. 4, addressing sentence after the attention
+ *     equation; P1 sec. 5, Fig. 7).  Entries past the last used one are never
+ *     read (the Python side pads with -1).
+ *   - context_lens: int32 [num_seqs]; tokens in each sequence INCLUDING the
+ *     tokens of the current step (the attention sums run up to the query's own
+ *     position, P1 sec. 4 attention equation).
+ *   - Start-location arrays (q_start_loc, write_start_loc): int32 [num_seqs+1],
+ *     exclusive prefix sums of per-sequence token counts; row r of a
+ *     [num_tokens][...] tensor belongs to sequence s when
+ *     loc[s] <= r < loc[s+1].  NULL means one token per sequence
+ *     (num_tokens == num_seqs, row s belongs to sequence s).  The n tokens of
+ *     sequence s are its last n: token i sits at position context_lens[s]-n+i.
+ *   - stream: a hipStream_t passed as void* (NULL = the null stream).  Every
+ *     call only enqueues work on it and returns; nothing synchronises.
+ *   - Supported shapes: dtype PA_F32 or PA_F16, head_dim 64 or 128,
+ *     block_size 8, 16 or 32, num_heads >= 1.
+ *   - Errors: problems visible from the host arguments return a negative
+ *     pa_status and launch nothing.  A failed launch returns PA_ERR_LAUNCH.
+ *     Device-resident contents are preconditions, not checked:
+ *     1 <= n_s <= context_lens[s] <= max_blocks_per_seq*block_size, table
+ *     entries of used blocks in [0, num_blocks), copy destinations distinct and
+ *     never a source.  The kernels clamp or skip anything that would address
+ *     memory outside the buffers described here, so a violated precondition
+ *     gives unspecified values, never an out-of-bounds access.
+ */
+#ifndef PAGED_KV_PA_H
+#define PAGED_KV_PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F32 = 0, PA_F16 = 1 } pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL                       */
+  PA_ERR_SHAPE = -2,       /* sizes out of range or inconsistent              */
+  PA_ERR_UNSUPPORTED = -3, /* dtype / head_dim / block_size not built         */
+  PA_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than required         */
+  PA_ERR_LAUNCH = -5       /* the HIP runtime rejected a kernel launch        */
+} pa_status;
+
+/*
+ * pa_write_kv — store this step's new K/V rows into their cache slots.
+ * Defined by the append step of the block manager (P2, pseudocode section:
+ * the new token's K and V go into the next slot of the last block) with the
+ * slot given by the block table (P1 sec. 5, Fig. 7).
+ *
+ * For every row t of k_new / v_new ([num_tokens][num_heads][head_dim] of
+ * dtype), belonging to sequence s as its i-th of n new tokens, position
+ * p = context_lens[s] - n + i is written to
+ *     k_pool[block_tables[s][p / block_size]][p % block_size][:][:]   (and v_pool)
+ * The copy is bit-exact.  Rows of different tokens must map to different
+ * slots (they do whenever the tables come from a block manager).
+ * num_tokens == 0 is a no-op.
+ */
+int pa_write_kv(void* k_pool, void* v_pool, int64_t num_blocks,
+                const void* k_new, const void* v_new,
+                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                const int32_t* context_lens, const int32_t* write_start_loc,
+                int32_t num_seqs, int32_t num_tokens,
+                int32_t num_heads, int32_t head_dim, int32_t block_size,
+                int32_t dtype, void* stream);
+
+/*
+ * pa_decode_workspace_bytes — bytes of device workspace pa_decode needs for
+ * a batch whose longest context is max_context_len (0 when no sequence is
+ * split into more than one context partition).  Host-only, never fails.
+ */
+size_t pa_decode_workspace_bytes(int32_t num_tokens, int32_t num_heads, int32_t head_dim,
+                                 int32_t max_context_len);
+
+/*
+ * pa_decode — paged attention: for every query row t (sequence s, position p)
+ * and head h,
+ *     out[t][h][:] = sum_{j<=p} softmax_j(q[t][h]·K_j[h] / sqrt(head_dim)) V_j[h]
+ * where K_j, V_j are token j's rows fetched through the block table
+ * (P1 sec. 4, attention equation and addressing; P2 section
+ * "PagedAttentionの仕組み", blockwise equation computed with online softmax).
+ * The scale is fixed at 1/sqrt(head_dim).
+ *
+ * q, out: [num_tokens][num_heads][head_dim] of dtype (out written in dtype,
+ *   rounded to nearest even from fp32 accumulation).
+ * q_start_loc: NULL for pure decode (one query per sequence); otherwise
+ *   sequences with n_s > 1 queries run the causal multi-query tile path
+ *   (chunked prefill mixed with decodes in one batch, P3 section
+ *   "Chunked prefill"), each query attending to positions <= its own.
+ * max_context_len, max_query_len: host copies of the maxima over the batch
+ *   (grid sizing); max_query_len > 1 requires dtype PA_F16.
+ * workspace: device scratch of at least
+ *   pa_decode_workspace_bytes(num_tokens, num_heads, head_dim, max_context_len)
+ *   bytes (NULL allowed when that is 0); contents on return are unspecified.
+ */
+int pa_decode(void* out, const void* q,
+              const void* k_pool, const void* v_pool, int64_t num_blocks,
+              const int32_t* block_tables, int32_t max_blocks_per_seq,
+              const int32_t* context_lens, const int32_t* q_start_loc,
+              int32_t num_seqs, int32_t num_tokens,
+              int32_t max_context_len, int32_t max_query_len,
+              int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t dtype,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_copy_blocks — copy-on-write block copies, batched: for every pair
+ * (src, dst) of block_pairs (int32 [num_pairs][2], device), the whole block
+ * k_pool[dst] = k_pool[src] and v_pool[dst] = v_pool[src], every slot filled
+ * or not, bit-exact (P2 pseudocode: copy_on_write copies the block's K and V
+ * tensors; P1 sec. 6, Fig. 9).  Destinations must be distinct and no
+ * destination may be a source.  num_pairs == 0 is a no-op.
+ */
+int pa_copy_blocks(void* k_pool, void* v_pool, int64_t num_blocks,
+                   const int32_t* block_pairs, int32_t num_pairs,
+                   int32_t num_heads, int32_t head_dim, int32_t block_size,
+                   int32_t dtype, void* stream);
+
+/* pa_strerror — static text for a pa_status value (never NULL). */
+const char* pa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_KV_PA_H */

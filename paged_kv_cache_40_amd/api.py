@@ -1,0 +1,120 @@
+"""Python binding of the C ABI (include/pa.h): same entry points, torch tensors in.
+
+Argument marshalling only: shapes and dtypes are read from the tensors, device
+pointers and the current HIP stream are passed through ctypes, and every step
+of the computation runs in the HIP kernels of libpagedkv.so.  A nonzero status
+raises RuntimeError with the library's message.
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.float32: _lib.PA_F32, torch.float16: _lib.PA_F16}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _require(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_pool(k_pool: torch.Tensor, v_pool: torch.Tensor):
+    _require(k_pool.dim() == 4 and k_pool.shape == v_pool.shape,
+             "k_pool / v_pool must be [num_blocks][block_size][num_heads][head_dim] alike")
+    _require(k_pool.dtype == v_pool.dtype and k_pool.dtype in _DTYPES, "pool dtype must be f32/f16")
+    _require(k_pool.is_cuda and v_pool.is_cuda, "pools must be on the GPU")
+    _require(k_pool.is_contiguous() and v_pool.is_contiguous(), "pools must be contiguous")
+    nb, bs, h, d = k_pool.shape
+    return nb, bs, h, d, _DTYPES[k_pool.dtype]
+
+
+def _check_index(t: Optional[torch.Tensor], name: str, n: Optional[int] = None):
+    if t is None:
+        return
+    _require(t.dtype == torch.int32 and t.is_cuda and t.is_contiguous(),
+             f"{name} must be a contiguous int32 GPU tensor")
+    if n is not None:
+        _require(t.shape[0] == n, f"{name} must have {n} rows")
+
+
+def pa_decode_workspace_bytes(num_tokens: int, num_heads: int, head_dim: int,
+                              max_context_len: int) -> int:
+    return int(_lib.load().pa_decode_workspace_bytes(num_tokens, num_heads, head_dim,
+                                                     max_context_len))
+
+
+def pa_write_kv(k_pool, v_pool, k_new, v_new, block_tables, context_lens,
+                write_start_loc=None, stream=None) -> None:
+    nb, bs, h, d, dt = _check_pool(k_pool, v_pool)
+    S = context_lens.shape[0]
+    _check_index(block_tables, "block_tables", S)
+    _check_index(context_lens, "context_lens")
+    _check_index(write_start_loc, "write_start_loc", S + 1)
+    T = k_new.shape[0]
+    _require(k_new.shape == v_new.shape == (T, h, d), "k_new / v_new must be [T][H][d]")
+    _require(k_new.dtype == v_new.dtype == k_pool.dtype, "k_new / v_new dtype must match the pool")
+    _require(k_new.is_contiguous() and v_new.is_contiguous(), "k_new / v_new must be contiguous")
+    st = _lib.load().pa_write_kv(
+        _ptr(k_pool), _ptr(v_pool), nb, _ptr(k_new), _ptr(v_new), _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), _ptr(write_start_loc), S, T, h, d, bs, dt,
+        _stream(stream))
+    _lib.check(st, "pa_write_kv")
+
+
+def pa_copy_blocks(k_pool, v_pool, block_pairs, stream=None) -> None:
+    nb, bs, h, d, dt = _check_pool(k_pool, v_pool)
+    _check_index(block_pairs, "block_pairs")
+    _require(block_pairs.dim() == 2 and block_pairs.shape[1] == 2, "block_pairs must be [n][2]")
+    st = _lib.load().pa_copy_blocks(_ptr(k_pool), _ptr(v_pool), nb, _ptr(block_pairs),
+                                    block_pairs.shape[0], h, d, bs, dt, _stream(stream))
+    _lib.check(st, "pa_copy_blocks")
+
+
+def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, q_start_loc=None,
+              max_context_len: Optional[int] = None, max_query_len: int = 1,
+              workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Attention of q over the paged context; writes and returns `out`.
+
+    max_context_len: host bound on context_lens (read from the device when omitted).
+    workspace: a uint8 GPU tensor of at least pa_decode_workspace_bytes(...) bytes
+    (allocated here when omitted).
+    """
+    nb, bs, h, d, dt = _check_pool(k_pool, v_pool)
+    S = context_lens.shape[0]
+    T = q.shape[0]
+    _check_index(block_tables, "block_tables", S)
+    _check_index(context_lens, "context_lens")
+    _check_index(q_start_loc, "q_start_loc", S + 1)
+    _require(q.shape == (T, h, d) and out.shape == q.shape, "q / out must be [T][H][d]")
+    _require(q.dtype == out.dtype == k_pool.dtype, "q / out dtype must match the pool")
+    _require(q.is_contiguous() and out.is_contiguous(), "q / out must be contiguous")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item())
+    need = pa_decode_workspace_bytes(T, h, d, max_context_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.load().pa_decode(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), nb, _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), _ptr(q_start_loc), S, T, int(max_context_len),
+        int(max_query_len), h, d, bs, dt, _ptr(workspace), ws_bytes, _stream(stream))
+    _lib.check(st, "pa_decode")
+    return out
+
+
+def pa_strerror(status: int) -> str:
+    return _lib.strerror(status)

@@ -1,0 +1,127 @@
+// C ABI of the paged KV-cache library: host-side argument checks, then the
+// launchers.  Every check here runs before any HIP call, so a rejected call
+// touches neither the device nor the stream.
+
+#include <math.h>
+
+#include "../../include/pa.h"
+#include "pa_internal.hpp"
+
+namespace {
+
+bool dtype_ok(int32_t dtype) { return dtype == PA_F32 || dtype == PA_F16; }
+int elt_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
+bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
+bool block_size_ok(int32_t b) { return b == 8 || b == 16 || b == 32; }
+
+// Shape checks common to every entry point; returns PA_OK or the first failure.
+int check_layout(int64_t num_blocks, int32_t num_heads, int32_t head_dim, int32_t block_size,
+                 int32_t dtype) {
+  if (num_blocks <= 0 || num_heads <= 0 || head_dim <= 0 || block_size <= 0) return PA_ERR_SHAPE;
+  if (!dtype_ok(dtype) || !head_dim_ok(head_dim) || !block_size_ok(block_size))
+    return PA_ERR_UNSUPPORTED;
+  // a token row (all heads) must be addressable with 32-bit element counts per block
+  if (static_cast<int64_t>(num_heads) * head_dim * block_size > (int64_t{1} << 30))
+    return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_strerror(int status) {
+  switch (status) {
+    case PA_OK: return "success";
+    case PA_ERR_NULL: return "a required pointer argument is NULL";
+    case PA_ERR_SHAPE: return "sizes out of range or inconsistent";
+    case PA_ERR_UNSUPPORTED: return "dtype, head_dim or block_size not supported";
+    case PA_ERR_WORKSPACE: return "workspace missing or smaller than pa_decode_workspace_bytes";
+    case PA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_tokens, int32_t num_heads, int32_t head_dim,
+                                 int32_t max_context_len) {
+  if (num_tokens <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+  return pa::decode_workspace_bytes(num_tokens, num_heads, head_dim, max_context_len);
+}
+
+int pa_write_kv(void* k_pool, void* v_pool, int64_t num_blocks, const void* k_new,
+                const void* v_new, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                const int32_t* context_lens, const int32_t* write_start_loc, int32_t num_seqs,
+                int32_t num_tokens, int32_t num_heads, int32_t head_dim, int32_t block_size,
+                int32_t dtype, void* stream) {
+  if (int st = check_layout(num_blocks, num_heads, head_dim, block_size, dtype)) return st;
+  if (num_seqs <= 0 || num_tokens < 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  if (write_start_loc == nullptr && num_tokens != num_seqs) return PA_ERR_SHAPE;
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size > INT32_MAX) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !block_tables || !context_lens) return PA_ERR_NULL;
+  const int64_t row_bytes = static_cast<int64_t>(num_heads) * head_dim * elt_bytes(dtype);
+  return launch_status(pa::launch_write_kv(
+      k_pool, v_pool, num_blocks, k_new, v_new, block_tables, max_blocks_per_seq, context_lens,
+      write_start_loc, num_seqs, num_tokens, row_bytes, block_size,
+      static_cast<hipStream_t>(stream)));
+}
+
+int pa_copy_blocks(void* k_pool, void* v_pool, int64_t num_blocks, const int32_t* block_pairs,
+                   int32_t num_pairs, int32_t num_heads, int32_t head_dim, int32_t block_size,
+                   int32_t dtype, void* stream) {
+  if (int st = check_layout(num_blocks, num_heads, head_dim, block_size, dtype)) return st;
+  if (num_pairs < 0) return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !block_pairs) return PA_ERR_NULL;
+  const int64_t block_bytes =
+      static_cast<int64_t>(block_size) * num_heads * head_dim * elt_bytes(dtype);
+  return launch_status(pa::launch_copy_blocks(k_pool, v_pool, num_blocks, block_pairs, num_pairs,
+                                              block_bytes, static_cast<hipStream_t>(stream)));
+}
+
+int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+              int64_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
+              const int32_t* context_lens, const int32_t* q_start_loc, int32_t num_seqs,
+              int32_t num_tokens, int32_t max_context_len, int32_t max_query_len,
+              int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t dtype,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  if (int st = check_layout(num_blocks, num_heads, head_dim, block_size, dtype)) return st;
+  if (num_seqs <= 0 || num_tokens <= 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  if (max_context_len <= 0 || max_query_len <= 0 || max_query_len > max_context_len)
+    return PA_ERR_SHAPE;
+  if (static_cast<int64_t>(max_context_len) >
+      static_cast<int64_t>(max_blocks_per_seq) * block_size)
+    return PA_ERR_SHAPE;
+  if (q_start_loc == nullptr && (num_tokens != num_seqs || max_query_len != 1))
+    return PA_ERR_SHAPE;
+  // grid limits of the decode launch: z = sequences, y = context partitions
+  if (num_seqs > 65535 || max_context_len / pa::kMinPartition >= 65535) return PA_ERR_SHAPE;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PA_ERR_NULL;
+  if (max_query_len > 1) return PA_ERR_UNSUPPORTED;  // multi-query tile path not built yet
+  const size_t need = pa::decode_workspace_bytes(num_tokens, num_heads, head_dim, max_context_len);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.num_blocks = num_blocks;
+  a.block_tables = block_tables;
+  a.max_blocks = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.q_start_loc = q_start_loc;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_heads = num_heads;
+  a.block_size = block_size;
+  a.max_context_len = max_context_len;
+  a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(head_dim)));
+  a.workspace = workspace;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return launch_status(pa::launch_decode(a, dtype, head_dim, block_size, max_context_len, st));
+}
+
+}  // extern "C"

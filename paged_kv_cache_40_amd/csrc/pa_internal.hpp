@@ -1,0 +1,73 @@
+// Host-side launchers behind the C ABI (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  int64_t num_blocks;
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  const int32_t* context_lens;
+  const int32_t* q_start_loc;
+  int32_t num_seqs;
+  int32_t num_tokens;
+  int32_t num_heads;
+  int32_t block_size;
+  int32_t max_context_len; // host bound; device context lengths are clamped to it
+  float scale_log2;        // log2(e) / sqrt(head_dim)
+  void* workspace;         // caller's scratch (see decode_workspace_bytes)
+  // set by the launcher:
+  int32_t num_parts_max;   // partition slots per (query row, head) in the workspace
+  int32_t part_size;       // tokens per context partition
+  float* ws_acc;           // [num_tokens][num_heads][num_parts_max][head_dim]
+  float* ws_ml;            // [num_tokens][num_heads][num_parts_max][2] = (max, sum), log2 domain
+};
+
+struct TileArgs {
+  void* out;
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  int64_t num_blocks;
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  const int32_t* context_lens;
+  const int32_t* q_start_loc;
+  int32_t num_seqs;
+  int32_t num_tokens;
+  int32_t num_heads;
+  int32_t tiles_per_seq;   // query tiles per sequence in the grid (from max_query_len)
+  float scale_log2;
+};
+
+// Smallest context partition any decode launch uses; sizes the workspace.
+constexpr int kMinPartition = 256;
+
+// Workspace bytes for the partial results of a decode launch (0 when no
+// sequence spans more than one partition).
+size_t decode_workspace_bytes(int64_t num_tokens, int64_t num_heads, int64_t head_dim,
+                              int64_t max_context_len);
+
+// dtype: 0 = fp32, 1 = fp16.  Return hipSuccess or the launch error.
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int block_size,
+                         int max_context_len, hipStream_t stream);
+hipError_t launch_tile(const TileArgs& a, int head_dim, int block_size, int max_query_len,
+                       hipStream_t stream);
+hipError_t launch_write_kv(void* k_pool, void* v_pool, int64_t num_blocks, const void* k_new,
+                           const void* v_new, const int32_t* block_tables, int32_t max_blocks,
+                           const int32_t* context_lens, const int32_t* write_start_loc,
+                           int32_t num_seqs, int32_t num_tokens, int64_t row_bytes,
+                           int32_t block_size, hipStream_t stream);
+hipError_t launch_copy_blocks(void* k_pool, void* v_pool, int64_t num_blocks,
+                              const int32_t* block_pairs, int32_t num_pairs, int64_t block_bytes,
+                              hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,129 @@
+"""The C-ABI library: it loads, exports every entry point include/pa.h declares,
+and rejects malformed host arguments with the documented status before any
+HIP call (so these run without a GPU; no kernel is launched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from paged_kv_cache_40_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from paged_kv_cache_40_amd.build import build
+        build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(pa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("pa_write_kv", "pa_decode", "pa_copy_blocks", "pa_decode_workspace_bytes",
+              "pa_strerror"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_binding_signatures_cover_header(lib):
+    from paged_kv_cache_40_amd import _lib
+    assert set(declared_functions()) == set(_lib.SIGNATURES)
+
+
+def test_strerror(lib):
+    for code in (0, -1, -2, -3, -4, -5, 7):
+        assert isinstance(lib.pa_strerror(code), bytes)
+    assert lib.pa_strerror(-4).startswith(b"workspace")
+
+
+def test_workspace_bytes(lib):
+    f = lib.pa_decode_workspace_bytes
+    assert f(256, 40, 128, 256) == 0               # one partition: no partials
+    assert f(256, 40, 128, 257) == 256 * 40 * 2 * 130 * 4
+    assert f(256, 40, 128, 4097) == 256 * 40 * 17 * 130 * 4
+    assert f(0, 40, 128, 4097) == 0
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails host validation first
+
+
+def write_kv(lib, **kw):
+    a = dict(k=FAKE, v=FAKE, nb=64, kn=FAKE, vn=FAKE, bt=FAKE, mb=8, cl=FAKE, wsl=None, S=4, T=4,
+             H=2, D=64, B=16, dt=0)
+    a.update(kw)
+    return lib.pa_write_kv(a["k"], a["v"], a["nb"], a["kn"], a["vn"], a["bt"], a["mb"], a["cl"],
+                           a["wsl"], a["S"], a["T"], a["H"], a["D"], a["B"], a["dt"], None)
+
+
+def decode(lib, **kw):
+    a = dict(o=FAKE, q=FAKE, k=FAKE, v=FAKE, nb=64, bt=FAKE, mb=8, cl=FAKE, qsl=None, S=4, T=4,
+             mcl=100, mql=1, H=2, D=64, B=16, dt=0, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.pa_decode(a["o"], a["q"], a["k"], a["v"], a["nb"], a["bt"], a["mb"], a["cl"],
+                         a["qsl"], a["S"], a["T"], a["mcl"], a["mql"], a["H"], a["D"], a["B"],
+                         a["dt"], a["ws"], a["wsb"], None)
+
+
+def copy_blocks(lib, **kw):
+    a = dict(k=FAKE, v=FAKE, nb=64, pairs=FAKE, n=3, H=2, D=64, B=16, dt=1)
+    a.update(kw)
+    return lib.pa_copy_blocks(a["k"], a["v"], a["nb"], a["pairs"], a["n"], a["H"], a["D"], a["B"],
+                              a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=None), -1), (dict(kn=None), -1), (dict(bt=None), -1), (dict(cl=None), -1),
+    (dict(D=96), -3), (dict(B=64), -3), (dict(dt=2), -3),
+    (dict(H=0), -2), (dict(nb=0), -2), (dict(S=0), -2), (dict(T=-1), -2), (dict(T=5), -2),
+    (dict(mb=0), -2),
+])
+def test_write_kv_rejects(lib, kw, code):
+    assert write_kv(lib, **kw) == code
+
+
+def test_write_kv_zero_tokens_is_a_noop(lib):
+    assert write_kv(lib, wsl=FAKE, T=0) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(o=None), -1), (dict(q=None), -1), (dict(v=None), -1), (dict(cl=None), -1),
+    (dict(D=32), -3), (dict(B=4), -3), (dict(dt=5), -3),
+    (dict(mcl=0), -2), (dict(mql=0), -2), (dict(mcl=129), -2), (dict(T=5), -2), (dict(mql=2), -2),
+    (dict(S=0), -2), (dict(H=-1), -2), (dict(mql=101), -2),
+    (dict(ws=None, mcl=300, mb=32), -4), (dict(wsb=10, mcl=300, mb=32), -4),
+])
+def test_decode_rejects(lib, kw, code):
+    assert decode(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(pairs=None), -1), (dict(v=None), -1), (dict(n=-1), -2), (dict(D=100), -3),
+    (dict(nb=-5), -2),
+])
+def test_copy_blocks_rejects(lib, kw, code):
+    assert copy_blocks(lib, **kw) == code
+
+
+def test_copy_blocks_zero_pairs_is_a_noop(lib):
+    assert copy_blocks(lib, n=0, pairs=None) == 0
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    from paged_kv_cache_40_amd import _lib
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError):
+        _lib.load(str(tmp_path / "missing.so"))

@@ -12,5 +12,6 @@ from .configs import (  # noqa: F401
     Workload,
     make_config,
     make_small,
+    make_custom_decode,
     CONFIG_NAMES,
 )

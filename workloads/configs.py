@@ -327,6 +327,17 @@ def config5(seed=5, num_seqs=256, num_heads=40, min_len=1024, max_len=4096, num_
                             num_blocks, write_one=True, rng=rng)
 
 
+def make_custom_decode(seed, dtype, num_heads, head_dim, block_size, lens, num_blocks=None,
+                       write_one=False, q_scale=1.0, name="custom_decode"):
+    """One query per sequence with the given context lengths; tables from a random permutation
+    of a pool 1.25x the blocks needed (or num_blocks)."""
+    lens = np.asarray(lens, dtype=np.int32)
+    need = int(sum(_cdiv(int(L), block_size) for L in lens))
+    nb = num_blocks if num_blocks is not None else max(need + 2, _cdiv(5 * need, 4))
+    return _decode_workload(name, seed, dtype, num_heads, head_dim, block_size, lens, nb,
+                            write_one=write_one, q_scale=q_scale)
+
+
 _MAKERS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 
