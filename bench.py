@@ -132,7 +132,7 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=5)
-    ap.add_argument("--cpu-seqs", type=int, default=48, help="oracle sample size (0 = skip)")
+    ap.add_argument("--cpu-seqs", type=int, default=256, help="oracle sample size (0 = skip)")
     ap.add_argument("--cpu-workers", type=int, default=0, help="0 = min(16, host cores)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (PMC byte calibration)")

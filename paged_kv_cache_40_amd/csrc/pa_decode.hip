@@ -14,64 +14,121 @@
 //   m = max_p m_p;  o = sum_p 2^(m_p - m) acc_p / sum_p 2^(m_p - m) l_p.
 //
 // Pass 1: one 64-lane workgroup per (sequence, head, partition of P tokens).
-//   * A token's head row (d elements) is split over kLpt lanes, 64 bytes
-//     each, fetched as four 16-byte loads arranged so that the kLpt lanes of
-//     a token read contiguous 16*kLpt-byte segments per instruction; one
-//     iteration covers kTpi = 64/kLpt tokens, a trip covers kU iterations and
-//     issues all of its K and V loads before using any of them.
-//   * q.k: v_dot2_f32_f16 (fp16) or fma (fp32) over the lane's 64 bytes, then a
-//     DPP sum over the token's kLpt lanes (quad_perm / row mirrors).
+//   * Lane layout: lane = 8*g + c.  Each load instruction reads one 128-byte
+//     cache line of 8 consecutive tokens' head rows: lane (g, c) takes the
+//     16 bytes at column c of token g's line.  A head row of kRow bytes spans
+//     kCpt = kRow/128 lines, so a lane holds kCpt 16-byte chunks per token
+//     and covers kR = 4/kCpt tokens per iteration (four K loads and four V
+//     loads per lane per iteration, 8*kR tokens).  A trip covers kU
+//     iterations and issues all of its K and V loads before using any.
+//   * The 8 tokens of one load share a block (block sizes are multiples of
+//     8), so each block id is a wave-uniform readlane from the partition's
+//     table entries, loaded once (one per lane).
+//   * q.k: v_dot2_f32_f16 (fp16) or fma (fp32) over the lane's chunks, then a
+//     DPP sum over the token's 8 lanes (quad_perm xor 1, xor 2, half-row mirror).
 //   * Softmax runs in the log2 domain (scores pre-multiplied by log2(e)/sqrt(d),
 //     v_exp_f32).  Each lane keeps (m, l, acc) for its own token positions;
 //     the running reference m only moves when some lane sees a score more
 //     than kTau above it (a wave vote), since any reference gives the same
 //     ratio and exponents stay below 2^kTau.
-//   * At the end the lanes are merged to one (m, l, acc[d]); a sequence with a
-//     single partition writes the normalised output directly.
+//   * At the end the 8 token groups are merged (xor 8, 16, 32) to one
+//     (m, l, acc[d]); a sequence with a single partition writes the
+//     normalised output directly.
 // Pass 2: one 64-lane workgroup per (sequence, head) with more than one
 //   partition merges the partials and writes out.
 //
-// Block ids of a partition are loaded once (one per lane) and broadcast with
-// readlane / bpermute.  All pool offsets are 64-bit.  Context lengths are
-// clamped to the table width and block ids outside [0, num_blocks) are
+// All pool offsets are 64-bit.  Context lengths are clamped to the table
+// width and to the host bound, and block ids outside [0, num_blocks) are
 // replaced by block 0, so malformed device data cannot address memory
-// outside the pools.
+// outside the pools or the workspace.
 
 #include <math.h>
 
 #include "pa_common.hpp"
 #include "pa_internal.hpp"
 
+// Build-time tuning knobs (defaults are the measured best on MI355X).
+#ifndef PA_DECODE_PARTITION
+#define PA_DECODE_PARTITION 0  // 0: chosen per launch (see pick_partition); else forced
+#endif
+#ifndef PA_DECODE_TRIP_U
+#define PA_DECODE_TRIP_U 0  // 0: 2 iterations per trip (1 when an iteration covers 32 tokens)
+#endif
+#ifndef PA_DECODE_NT_LOADS
+#define PA_DECODE_NT_LOADS 1  // K/V are read once: streaming (non-temporal) loads
+#endif
+#ifndef PA_DECODE_HEADS_PER_WG
+#define PA_DECODE_HEADS_PER_WG 4  // waves per workgroup, one head each
+#endif
+#ifndef PA_DECODE_BALANCED
+#define PA_DECODE_BALANCED 1  // 1: a sequence's partitions share its tokens evenly
+#endif
+#ifndef PA_DECODE_GRID_ORDER
+#define PA_DECODE_GRID_ORDER 2  // 2: head group fastest, then sequence, then partition
+#endif
+#ifndef PA_DECODE_WAVES_PER_EU
+#define PA_DECODE_WAVES_PER_EU 0  // 0: compiler's choice; n: ask for n waves per SIMD
+#endif
+#if PA_DECODE_WAVES_PER_EU > 0
+#define PA_DECODE_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES_PER_EU)))
+#else
+#define PA_DECODE_OCCUPANCY
+#endif
+
 namespace pa {
+
+static_assert(PA_DECODE_PARTITION == 0 || PA_DECODE_PARTITION >= kMinPartition,
+              "partition below the workspace sizing");
+
+__device__ __forceinline__ u32x4 ld_kv(const void* p) {
+#if PA_DECODE_NT_LOADS
+  return ld16_stream(p);
+#else
+  return ld16(p);
+#endif
+}
 
 template <typename T, int D, int BS, int P>
 struct DecodeCfg {
   static constexpr int kElt = sizeof(T);
   static constexpr int kRow = D * kElt;        // bytes of one head's row of one token
-  static constexpr int kLpt = kRow / 64;       // lanes per token (64 bytes each)
-  static constexpr int kTpi = kWave / kLpt;    // tokens per iteration
+  static constexpr int kCpt = kRow / 128;      // 16-byte chunks per lane per token
+  static constexpr int kR = 4 / kCpt;          // tokens per lane per iteration
+  static constexpr int kTpi = 8 * kR;          // tokens per iteration
   static constexpr int kEpc = 16 / kElt;       // elements per 16-byte chunk
-  static constexpr int kEpl = 4 * kEpc;        // elements per lane per token
-  static constexpr int kU = kTpi >= 32 ? 1 : 2;  // iterations per trip
+  static constexpr int kEpl = kCpt * kEpc;     // elements (head dims) per lane
+  static constexpr int kU = PA_DECODE_TRIP_U > 0 ? PA_DECODE_TRIP_U : 1;  // iterations per trip
+  static constexpr int kG = kU * kR;           // token groups per lane per trip
   static constexpr int kTrip = kU * kTpi;      // tokens per trip
   static constexpr int kBlocks = P / BS;       // table entries per partition
-  static constexpr bool kUniformBlock = (BS % kTpi) == 0;  // one block per iteration
-  static_assert(kLpt >= 2 && kLpt <= 8, "row must span 2..8 lanes");
+  static constexpr int kTabRegs = (kBlocks + kWave - 1) / kWave;  // table entries per lane
+  static constexpr int kAlign = kTrip > BS ? kTrip : BS;  // partition starts are multiples
+  static_assert(kCpt >= 1 && kCpt <= 4 && 4 % kCpt == 0, "head row must be 1, 2 or 4 lines");
+  static_assert(BS % 8 == 0, "a load's 8 tokens must share a block");
   static_assert(P % kTrip == 0 && P % BS == 0, "partition must hold whole trips and blocks");
-  static_assert(kBlocks <= kWave, "one table entry per lane");
+  static_assert(kTabRegs <= 2, "at most two table entries per lane");
 };
 
 constexpr float kTau = 8.0f;  // log2 headroom before the running reference moves
 
+constexpr int kHeadsPerWg = PA_DECODE_HEADS_PER_WG;
+
 template <typename T, int D, int BS, int P>
-__global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kHeadsPerWg) PA_DECODE_OCCUPANCY
+void decode_partition_kernel(DecodeArgs a) {
   using C = DecodeCfg<T, D, BS, P>;
-  const int h = blockIdx.x;
-  const int part = blockIdx.y;
-  const int s = blockIdx.z;
-  const int lane = threadIdx.x;
-  const int tok = lane / C::kLpt;
-  const int c = lane % C::kLpt;
+#if PA_DECODE_GRID_ORDER == 1
+  const int part = blockIdx.x, hg = blockIdx.y, s = blockIdx.z;
+#elif PA_DECODE_GRID_ORDER == 2
+  const int hg = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
+#else
+  const int hg = blockIdx.x, part = blockIdx.y, s = blockIdx.z;
+#endif
+  const int h = hg * kHeadsPerWg + static_cast<int>(threadIdx.x >> 6);
+  if (h >= a.num_heads) return;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 3;  // token within a group of 8
+  const int c = lane & 7;   // 16-byte column within a 128-byte line
 
   int qrow = s;
   if (a.q_start_loc != nullptr) {
@@ -81,38 +138,65 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   }
   if (qrow < 0 || qrow >= a.num_tokens) return;
   const int ctx = min(a.context_lens[s], min(a.max_blocks * BS, a.max_context_len));
-  const int start = part * P;
-  if (start >= ctx) return;
-  const int ntok = min(P, ctx - start);
   const int nparts = (ctx + P - 1) / P;
+#if PA_DECODE_BALANCED
+  // equal shares (rounded up to whole trips and blocks), so no partition is a short tail
+  const int share = ((ctx + nparts - 1) / nparts + C::kAlign - 1) / C::kAlign * C::kAlign;
+#else
+  const int share = P;
+#endif
+  const int start = part * share;
+  if (start >= ctx) {
+    // Rounded-up shares can leave a trailing partition without tokens; the merge pass
+    // still reads it, so it records an empty partial (m = -inf, l = 0, acc = 0).
+    if (part < nparts && (threadIdx.x & 63) < 8) {
+      const int64_t slot = (static_cast<int64_t>(qrow) * a.num_heads + h) * a.num_parts_max + part;
+      float* wp = a.ws_acc + slot * D;
+      for (int e = (threadIdx.x & 7) * 4; e < D; e += 32)
+        st16(wp + e, u32x4{0, 0, 0, 0});
+      if ((threadIdx.x & 63) == 0) {
+        a.ws_ml[slot * 2] = -INFINITY;
+        a.ws_ml[slot * 2 + 1] = 0.f;
+      }
+    }
+    return;
+  }
+  const int ntok = min(share, ctx - start);
 
   const int64_t row_stride = static_cast<int64_t>(a.num_heads) * D;
+  // element offset of this lane's chunk j inside a head row
+  auto col = [&](int j) { return (j * 8 + c) * C::kEpc; };
   const T* kbase = static_cast<const T*>(a.k_pool) + static_cast<int64_t>(h) * D;
   const T* vbase = static_cast<const T*>(a.v_pool) + static_cast<int64_t>(h) * D;
 
-  // this lane's four chunks of q
   const T* qp = static_cast<const T*>(a.q) + (static_cast<int64_t>(qrow) * a.num_heads + h) * D;
-  u32x4 qc[4];
+  u32x4 qc[C::kCpt];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) qc[k] = ld16(qp + (k * C::kLpt + c) * C::kEpc);
+  for (int j = 0; j < C::kCpt; ++j) qc[j] = ld16(qp + col(j));
 
   // physical blocks of this partition, one per lane
   const int32_t* btrow = a.block_tables + static_cast<int64_t>(s) * a.max_blocks + start / BS;
   const int nblk = (ntok + BS - 1) / BS;
-  int my_blk = 0;
-  if (lane < nblk) {
-    const int b = btrow[lane];
-    my_blk = (b >= 0 && b < a.num_blocks) ? b : 0;
-  }
-
-  auto token_offset = [&](int jrel) -> int64_t {
-    int blk;
-    if constexpr (C::kUniformBlock) {
-      blk = __builtin_amdgcn_readlane(my_blk, __builtin_amdgcn_readfirstlane(jrel / BS));
-    } else {
-      blk = __shfl(my_blk, jrel / BS, kWave);
+  int my_blk[C::kTabRegs];
+#pragma unroll
+  for (int r = 0; r < C::kTabRegs; ++r) {
+    my_blk[r] = 0;
+    if (r * kWave + lane < nblk) {
+      const int b = btrow[r * kWave + lane];
+      my_blk[r] = (b >= 0 && b < a.num_blocks) ? b : 0;
     }
-    return (static_cast<int64_t>(blk) * BS + (jrel % BS)) * row_stride;
+  }
+  // row offset of token (group_base + g), where group_base is a multiple of 8 (wave-uniform)
+  auto row_offset = [&](int group_base) -> int64_t {
+    const int bi = group_base / BS;
+    int blk;
+    if constexpr (C::kTabRegs == 1) {
+      blk = __builtin_amdgcn_readlane(my_blk[0], bi);
+    } else {
+      blk = bi < kWave ? __builtin_amdgcn_readlane(my_blk[0], bi)
+                       : __builtin_amdgcn_readlane(my_blk[C::kTabRegs - 1], bi - kWave);
+    }
+    return (static_cast<int64_t>(blk) * BS + (group_base % BS) + g) * row_stride;
   };
 
   float m = -INFINITY, l = 0.f;
@@ -120,10 +204,11 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
   for (int e = 0; e < C::kEpl; ++e) acc[e] = 0.f;
 
-  auto update = [&](const float (&sc)[C::kU], const u32x4 (&vr)[C::kU][4], const bool (&ok)[C::kU]) {
+  auto update = [&](const float (&sc)[C::kG], const u32x4 (&vr)[C::kG][C::kCpt],
+                    const bool (&ok)[C::kG]) {
     float mx = sc[0];
 #pragma unroll
-    for (int u = 1; u < C::kU; ++u) mx = fmaxf(mx, sc[u]);
+    for (int i = 1; i < C::kG; ++i) mx = fmaxf(mx, sc[i]);
     if (__any(mx > m + kTau)) {
       const float mn = fmaxf(m, mx);
       const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m - mn);
@@ -133,111 +218,113 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
       m = mn;
     }
 #pragma unroll
-    for (int u = 0; u < C::kU; ++u) {
-      const float p = ok[u] ? fast_exp2(sc[u] - m) : 0.f;
+    for (int i = 0; i < C::kG; ++i) {
+      const float p = ok[i] ? fast_exp2(sc[i] - m) : 0.f;
       l += p;
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
+      for (int j = 0; j < C::kCpt; ++j)
 #pragma unroll
         for (int e = 0; e < C::kEpc; ++e)
-          acc[k * C::kEpc + e] = fmaf(p, chunk_elt<T>(vr[u][k], e), acc[k * C::kEpc + e]);
+          acc[j * C::kEpc + e] = fmaf(p, chunk_elt<T>(vr[i][j], e), acc[j * C::kEpc + e]);
     }
+  };
+
+  auto score = [&](const u32x4 (&kr)[C::kCpt]) {
+    float d = 0.f;
+#pragma unroll
+    for (int j = 0; j < C::kCpt; ++j) d = chunk_dot<T>(qc[j], kr[j], d);
+    return group_sum<8>(d) * a.scale_log2;
   };
 
   const int full = ntok / C::kTrip;
   for (int trip = 0; trip < full; ++trip) {
-    u32x4 kr[C::kU][4], vr[C::kU][4];
-    int64_t off[C::kU];
+    u32x4 kr[C::kG][C::kCpt], vr[C::kG][C::kCpt];
+    int64_t off[C::kG];
 #pragma unroll
-    for (int u = 0; u < C::kU; ++u) {
-      off[u] = token_offset((trip * C::kU + u) * C::kTpi + tok);
+    for (int i = 0; i < C::kG; ++i) {
+      off[i] = row_offset(trip * C::kTrip + i * 8);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) kr[u][k] = ld16(kbase + off[u] + (k * C::kLpt + c) * C::kEpc);
+      for (int j = 0; j < C::kCpt; ++j) kr[i][j] = ld_kv(kbase + off[i] + col(j));
     }
 #pragma unroll
-    for (int u = 0; u < C::kU; ++u)
+    for (int i = 0; i < C::kG; ++i)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) vr[u][k] = ld16(vbase + off[u] + (k * C::kLpt + c) * C::kEpc);
-    float sc[C::kU];
-    bool ok[C::kU];
+      for (int j = 0; j < C::kCpt; ++j) vr[i][j] = ld_kv(vbase + off[i] + col(j));
+    float sc[C::kG];
+    bool ok[C::kG];
 #pragma unroll
-    for (int u = 0; u < C::kU; ++u) {
-      float d = 0.f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) d = chunk_dot<T>(qc[k], kr[u][k], d);
-      sc[u] = group_sum<C::kLpt>(d) * a.scale_log2;
-      ok[u] = true;
+    for (int i = 0; i < C::kG; ++i) {
+      sc[i] = score(kr[i]);
+      ok[i] = true;
     }
     update(sc, vr, ok);
   }
 
   if (full * C::kTrip < ntok) {  // ragged last trip: lanes past the end load nothing
-    u32x4 kr[C::kU][4], vr[C::kU][4];
-    bool ok[C::kU];
-    int64_t off[C::kU];
+    u32x4 kr[C::kG][C::kCpt], vr[C::kG][C::kCpt];
+    bool ok[C::kG];
 #pragma unroll
-    for (int u = 0; u < C::kU; ++u) {
-      const int jrel = (full * C::kU + u) * C::kTpi + tok;
-      ok[u] = jrel < ntok;
-      off[u] = token_offset(ok[u] ? jrel : 0);
+    for (int i = 0; i < C::kG; ++i) {
+      const int base = full * C::kTrip + i * 8;
+      ok[i] = base + g < ntok;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        kr[u][k] = u32x4{0, 0, 0, 0};
-        vr[u][k] = u32x4{0, 0, 0, 0};
+      for (int j = 0; j < C::kCpt; ++j) {
+        kr[i][j] = u32x4{0, 0, 0, 0};
+        vr[i][j] = u32x4{0, 0, 0, 0};
       }
-      if (ok[u]) {
+      if (base < ntok) {  // wave-uniform: the group has at least one valid token
+        const int64_t off = row_offset(base);
+        if (ok[i]) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) kr[u][k] = ld16(kbase + off[u] + (k * C::kLpt + c) * C::kEpc);
+          for (int j = 0; j < C::kCpt; ++j) kr[i][j] = ld_kv(kbase + off + col(j));
 #pragma unroll
-        for (int k = 0; k < 4; ++k) vr[u][k] = ld16(vbase + off[u] + (k * C::kLpt + c) * C::kEpc);
+          for (int j = 0; j < C::kCpt; ++j) vr[i][j] = ld_kv(vbase + off + col(j));
+        }
       }
     }
-    float sc[C::kU];
+    float sc[C::kG];
 #pragma unroll
-    for (int u = 0; u < C::kU; ++u) {
-      float d = 0.f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) d = chunk_dot<T>(qc[k], kr[u][k], d);
-      d = group_sum<C::kLpt>(d) * a.scale_log2;
-      sc[u] = ok[u] ? d : -INFINITY;
+    for (int i = 0; i < C::kG; ++i) {
+      const float d = score(kr[i]);
+      sc[i] = ok[i] ? d : -INFINITY;
     }
     update(sc, vr, ok);
   }
 
-  // merge the lanes: common reference, then sum over the token lanes of each chunk index
+  // merge the 8 token groups: common reference, then sum over lanes of equal column c
   const float M = wave_max(m);
   const float f = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
   l *= f;
 #pragma unroll
   for (int e = 0; e < C::kEpl; ++e) acc[e] *= f;
 #pragma unroll
-  for (int x = C::kLpt; x < kWave; x <<= 1) {
+  for (int x = 8; x < kWave; x <<= 1) {
     l += shfl_xor_f(l, x);
 #pragma unroll
     for (int e = 0; e < C::kEpl; ++e) acc[e] += shfl_xor_f(acc[e], x);
   }
 
-  if (tok != 0) return;
+  if (g != 0) return;
   if (nparts == 1) {
     const float inv = 1.f / l;
     T* op = static_cast<T*>(a.out) + (static_cast<int64_t>(qrow) * a.num_heads + h) * D;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int j = 0; j < C::kCpt; ++j) {
       float v[C::kEpc];
 #pragma unroll
-      for (int e = 0; e < C::kEpc; ++e) v[e] = acc[k * C::kEpc + e] * inv;
-      store_chunk<T>(op + (k * C::kLpt + c) * C::kEpc, v);
+      for (int e = 0; e < C::kEpc; ++e) v[e] = acc[j * C::kEpc + e] * inv;
+      store_chunk<T>(op + col(j), v);
     }
   } else {
     const int64_t slot = (static_cast<int64_t>(qrow) * a.num_heads + h) * a.num_parts_max + part;
     float* wp = a.ws_acc + slot * D;
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+    for (int j = 0; j < C::kCpt; ++j)
 #pragma unroll
       for (int e4 = 0; e4 < C::kEpc; e4 += 4) {
-        f32x4 v = {acc[k * C::kEpc + e4], acc[k * C::kEpc + e4 + 1], acc[k * C::kEpc + e4 + 2],
-                   acc[k * C::kEpc + e4 + 3]};
-        st16(wp + (k * C::kLpt + c) * C::kEpc + e4, __builtin_bit_cast(u32x4, v));
+        f32x4 v = {acc[j * C::kEpc + e4], acc[j * C::kEpc + e4 + 1], acc[j * C::kEpc + e4 + 2],
+                   acc[j * C::kEpc + e4 + 3]};
+        st16(wp + col(j) + e4, __builtin_bit_cast(u32x4, v));
       }
     if (c == 0) {
       a.ws_ml[slot * 2] = M;
@@ -296,10 +383,19 @@ static hipError_t launch_decode_t(const DecodeArgs& a0, int max_context_len, hip
   a.part_size = P;
   const int nparts = (max_context_len + P - 1) / P;
   a.num_parts_max = nparts;
+  // ws_ml follows ws_acc; both fit the workspace sized for kMinPartition-token partitions
   a.ws_acc = static_cast<float*>(a.workspace);
   a.ws_ml = a.ws_acc + static_cast<int64_t>(a.num_tokens) * a.num_heads * nparts * D;
-  dim3 grid1(a.num_heads, nparts, a.num_seqs);
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, BS, P>), grid1, dim3(kWave), 0, stream, a);
+  const int hgroups = (a.num_heads + kHeadsPerWg - 1) / kHeadsPerWg;
+#if PA_DECODE_GRID_ORDER == 1
+  dim3 grid1(nparts, hgroups, a.num_seqs);
+#elif PA_DECODE_GRID_ORDER == 2
+  dim3 grid1(hgroups, a.num_seqs, nparts);
+#else
+  dim3 grid1(hgroups, nparts, a.num_seqs);
+#endif
+  hipLaunchKernelGGL((decode_partition_kernel<T, D, BS, P>), grid1, dim3(kWave * kHeadsPerWg), 0,
+                     stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nparts <= 1) return err;
   dim3 grid2(a.num_heads, a.num_seqs);
@@ -307,13 +403,39 @@ static hipError_t launch_decode_t(const DecodeArgs& a0, int max_context_len, hip
   return hipGetLastError();
 }
 
+// Largest partition (fewest partial results) that still gives the launch enough waves
+// to fill the chip: sequences x heads x partitions of the longest context >= kTargetWaves.
+// The table preload holds at most 128 block ids, which caps the partition for B = 8.
+constexpr int64_t kTargetWaves = 16384;
+
+static int pick_partition(const DecodeArgs& a, int block_size, int max_context_len) {
+  if (PA_DECODE_PARTITION > 0) return PA_DECODE_PARTITION;
+  const int cap = block_size == 8 ? 1024 : 2048;
+  const int64_t units = static_cast<int64_t>(a.num_seqs) * a.num_heads;
+  int p = cap;
+  while (p > kMinPartition && units * ((max_context_len + p - 1) / p) < kTargetWaves) p >>= 1;
+  return p;
+}
+
+template <typename T, int D, int BS>
+static hipError_t launch_decode_p(const DecodeArgs& a, int max_context_len, hipStream_t stream) {
+  const int p = pick_partition(a, BS, max_context_len);
+  constexpr int kCapP = BS == 8 ? 1024 : 2048;
+  switch (p < kCapP ? p : kCapP) {
+    case 256: return launch_decode_t<T, D, BS, 256>(a, max_context_len, stream);
+    case 512: return launch_decode_t<T, D, BS, 512>(a, max_context_len, stream);
+    case 1024: return launch_decode_t<T, D, BS, 1024>(a, max_context_len, stream);
+    default: return launch_decode_t<T, D, BS, kCapP>(a, max_context_len, stream);
+  }
+}
+
 template <typename T, int D>
 static hipError_t launch_decode_bs(const DecodeArgs& a, int block_size, int max_context_len,
                                    hipStream_t stream) {
   switch (block_size) {
-    case 8: return launch_decode_t<T, D, 8, kMinPartition>(a, max_context_len, stream);
-    case 16: return launch_decode_t<T, D, 16, kMinPartition>(a, max_context_len, stream);
-    case 32: return launch_decode_t<T, D, 32, kMinPartition>(a, max_context_len, stream);
+    case 8: return launch_decode_p<T, D, 8>(a, max_context_len, stream);
+    case 16: return launch_decode_p<T, D, 16>(a, max_context_len, stream);
+    case 32: return launch_decode_p<T, D, 32>(a, max_context_len, stream);
     default: return hipErrorInvalidValue;
   }
 }

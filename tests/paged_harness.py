@@ -82,7 +82,12 @@ def assert_bits_equal(a, b, what: str = "") -> None:
 
 def snapshot_for(w, t, seqs):
     """Host copies of every block the sampled sequences read (plus copy sources), taken from
-    the freshly generated device pools.  Returns a compact sub-problem for the oracle."""
+    the freshly generated device pools: a compact sub-problem for the oracle.
+
+    Other sequences that share a block with the sample and append tokens this step are
+    carried along as write-only sequences, so their writes into shared blocks are modelled
+    too; their blocks outside the sample map to one extra scratch block (never compared).
+    """
     B = w.block_size
     nb = -(-w.context_lens.astype(np.int64) // B)
     blocks = []
@@ -95,20 +100,28 @@ def snapshot_for(w, t, seqs):
         blocks += [a for a, _ in pairs]
     uniq = sorted(set(blocks))
     remap = {b: i for i, b in enumerate(uniq)}
+    scratch = len(uniq)
+    writers = []
+    if w.num_writes:
+        inset = set(uniq)
+        writers = [s for s in range(w.num_seqs) if s not in seqs and w.write_lens[s] > 0
+                   and inset.intersection(int(x) for x in w.block_tables[s, :nb[s]])]
+    all_seqs = list(seqs) + writers
     idx = torch.tensor(uniq, dtype=torch.int64, device=t["k_pool"].device)
-    kp = t["k_pool"].index_select(0, idx).cpu().numpy()
-    vp = t["v_pool"].index_select(0, idx).cpu().numpy()
-    width = int(nb[list(seqs)].max())
-    bt = np.full((len(seqs), width), -1, np.int32)
-    for i, s in enumerate(seqs):
-        bt[i, :nb[s]] = [remap[int(x)] for x in w.block_tables[s, :nb[s]]]
+    pad = torch.full((1,) + tuple(t["k_pool"].shape[1:]), float("nan"), dtype=t["k_pool"].dtype)
+    kp = torch.cat([t["k_pool"].index_select(0, idx).cpu(), pad]).numpy()
+    vp = torch.cat([t["v_pool"].index_select(0, idx).cpu(), pad]).numpy()
+    width = int(nb[all_seqs].max())
+    bt = np.full((len(all_seqs), width), -1, np.int32)
+    for i, s in enumerate(all_seqs):
+        bt[i, :nb[s]] = [remap.get(int(x), scratch) for x in w.block_tables[s, :nb[s]]]
     qsl = w.q_start_loc()
     wsl = w.write_start_loc()
     q_all = t["q"]
     q_rows = [np.arange(qsl[s], qsl[s + 1]) if qsl is not None else np.asarray([s]) for s in seqs]
     sub = dict(
-        k_pool=kp, v_pool=vp, block_tables=bt, uniq=uniq,
-        context_lens=w.context_lens[list(seqs)].astype(np.int32),
+        k_pool=kp, v_pool=vp, block_tables=bt, uniq=uniq, num_attn=len(seqs),
+        context_lens=w.context_lens[all_seqs].astype(np.int32),
         q=q_all[torch.from_numpy(np.concatenate(q_rows)).to(q_all.device)].cpu().numpy(),
         q_rows=q_rows,
         q_start_loc=np.concatenate([[0], np.cumsum([len(r) for r in q_rows])]).astype(np.int32),
@@ -116,7 +129,7 @@ def snapshot_for(w, t, seqs):
     )
     if w.num_writes:
         w_rows = [np.arange(wsl[s], wsl[s + 1]) if wsl is not None else np.asarray([s])
-                  for s in seqs]
+                  for s in all_seqs]
         rows = torch.from_numpy(np.concatenate(w_rows)).to(q_all.device)
         sub["k_new"] = t["k_new"][rows].cpu().numpy()
         sub["v_new"] = t["v_new"][rows].cpu().numpy()
@@ -126,6 +139,8 @@ def snapshot_for(w, t, seqs):
 
 
 def oracle_sub(w, sub, heads=None):
+    """Oracle copy -> write -> attention on a compact sub-problem.  Returns the per-sequence
+    outputs of the sampled sequences and the compact pools without the scratch block."""
     kp, vp = sub["k_pool"], sub["v_pool"]
     if len(sub["copy_pairs"]):
         kp, vp = oracle.copy_blocks(kp, vp, sub["copy_pairs"])
@@ -134,11 +149,11 @@ def oracle_sub(w, sub, heads=None):
                                  sub["context_lens"], w.block_size, sub["write_start_loc"])
     outs = []
     qsl = sub["q_start_loc"]
-    for i in range(len(sub["context_lens"])):
+    for i in range(sub["num_attn"]):
         outs.append(oracle.paged_attention_seq(sub["q"][qsl[i]:qsl[i + 1]], kp, vp,
                                                sub["block_tables"][i], int(sub["context_lens"][i]),
                                                w.block_size, heads=heads))
-    return outs, kp, vp
+    return outs, kp[:-1], vp[:-1]
 
 
 def pick_sequences(w, n=4, seed=0):

@@ -263,3 +263,31 @@ def test_side_stream_and_reused_workspace():
     ref, _, _ = oracle_step(w, h)
     assert_close(out.cpu().numpy(), ref, w.dtype, "side stream")
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+# Batch shapes that make the launch pick each context-partition size (the largest of
+# 2048/1024/512/256 tokens that still gives >= 16384 waves), checked on sampled sequences.
+@pytest.mark.parametrize("S,H,lo,hi,B,expect_p", [
+    (64, 40, 3000, 4096, 16, 256),
+    (128, 32, 2049, 4096, 16, 512),
+    (128, 32, 3073, 4096, 32, 1024),
+    (256, 40, 4097, 6000, 16, 2048),
+    (192, 40, 2049, 4096, 8, 1024),
+])
+def test_partition_sizes_sampled(S, H, lo, hi, B, expect_p):
+    rng = np.random.default_rng(S + H + B)
+    lens = rng.integers(lo, hi + 1, size=S)
+    lens[0], lens[-1] = lo, hi
+    w = make_custom_decode(17, "f16", H, 128, B, lens, write_one=True,
+                           name=f"partition_{expect_p}_B{B}")
+    log(f"[case] {w.name} S={S} H={H} L=[{lo},{hi}] NB={w.num_blocks}")
+    t = w.device_tensors("cuda")
+    seqs = pick_sequences(w, n=3, seed=S)
+    sub = snapshot_for(w, t, seqs)
+    out = run_library(w, t)
+    torch.cuda.synchronize()
+    refs, kp, _ = oracle_sub(w, sub)
+    for i, s in enumerate(seqs):
+        assert_close(out[s:s + 1].cpu().numpy(), refs[i], w.dtype, f"{w.name} seq {s}")
+    idx_t = torch.tensor(sub["uniq"], dtype=torch.int64, device="cuda")
+    assert_bits_equal(t["k_pool"].index_select(0, idx_t).cpu().numpy(), kp, "k_pool sampled")
