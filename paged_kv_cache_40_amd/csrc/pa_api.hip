@@ -99,7 +99,9 @@ int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
   // grid limits of the decode launch: z = sequences, y = context partitions
   if (num_seqs > 65535 || max_context_len / pa::kMinPartition >= 65535) return PA_ERR_SHAPE;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PA_ERR_NULL;
-  if (max_query_len > 1) return PA_ERR_UNSUPPORTED;  // multi-query tile path not built yet
+  // the multi-query tile path is built for fp16 with head_dim 128
+  if (max_query_len > 1 && (dtype != PA_F16 || head_dim != 128)) return PA_ERR_UNSUPPORTED;
+  if (max_query_len > 1 && (max_query_len + 63) / 64 > 65535) return PA_ERR_SHAPE;
   const size_t need = pa::decode_workspace_bytes(num_tokens, num_heads, head_dim, max_context_len);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_WORKSPACE;
 
@@ -121,7 +123,25 @@ int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
   a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(head_dim)));
   a.workspace = workspace;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return launch_status(pa::launch_decode(a, dtype, head_dim, block_size, max_context_len, st));
+  // single-query sequences: context partitions + merge; the kernels skip the others
+  int status = launch_status(pa::launch_decode(a, dtype, head_dim, block_size, max_context_len, st));
+  if (status != PA_OK || max_query_len <= 1) return status;
+  // sequences with several queries: causal MFMA tiles
+  pa::TileArgs ta{};
+  ta.out = out;
+  ta.q = q;
+  ta.k_pool = k_pool;
+  ta.v_pool = v_pool;
+  ta.num_blocks = num_blocks;
+  ta.block_tables = block_tables;
+  ta.max_blocks = max_blocks_per_seq;
+  ta.context_lens = context_lens;
+  ta.q_start_loc = q_start_loc;
+  ta.num_seqs = num_seqs;
+  ta.num_tokens = num_tokens;
+  ta.num_heads = num_heads;
+  ta.scale_log2 = a.scale_log2;
+  return launch_status(pa::launch_tile(ta, head_dim, block_size, max_query_len, st));
 }
 
 }  // extern "C"

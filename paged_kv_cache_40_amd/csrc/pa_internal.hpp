@@ -44,7 +44,6 @@ struct TileArgs {
   int32_t num_seqs;
   int32_t num_tokens;
   int32_t num_heads;
-  int32_t tiles_per_seq;   // query tiles per sequence in the grid (from max_query_len)
   float scale_log2;
 };
 

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from paged_kv_cache_40_amd import api
-from workloads import make_config, make_small, make_custom_decode
+from workloads import make_config, make_small, make_custom_decode, make_custom_mixed
 from paged_harness import (assert_bits_equal, assert_close, host_copy, log, oracle_step,
                            oracle_sub, pick_sequences, run_library, snapshot_for)
 
@@ -41,7 +41,7 @@ def test_config1_tiny_fp32(seed):
     full_check(make_config(1, seed=seed))
 
 
-@pytest.mark.parametrize("idx", [2, 3, 5])
+@pytest.mark.parametrize("idx", [2, 3, 4, 5])
 @pytest.mark.parametrize("seed", [1, 2])
 def test_small_variants(idx, seed):
     full_check(make_small(idx, seed=seed))
@@ -52,7 +52,7 @@ def test_small_config2_peaked(q_scale):
     full_check(make_small(2, seed=5, q_scale=q_scale), f"q_scale={q_scale}")
 
 
-@pytest.mark.parametrize("idx", [2, 3, 5])
+@pytest.mark.parametrize("idx", [2, 3, 4, 5])
 def test_full_size_sampled(idx):
     """The full batch as bench.py runs it; the oracle recomputes sampled sequences (every head)
     and their blocks of the pools, plus a whole-pool check that only the expected slots moved."""
@@ -291,3 +291,26 @@ def test_partition_sizes_sampled(S, H, lo, hi, B, expect_p):
         assert_close(out[s:s + 1].cpu().numpy(), refs[i], w.dtype, f"{w.name} seq {s}")
     idx_t = torch.tensor(sub["uniq"], dtype=torch.int64, device="cuda")
     assert_bits_equal(t["k_pool"].index_select(0, idx_t).cpu().numpy(), kp, "k_pool sampled")
+
+
+# ------------------------------------------------ multi-query tile path --
+
+@pytest.mark.parametrize("B", [8, 16, 32])
+def test_chunk_tiles_edges(B):
+    """Chunks of 2..130 queries (one short of, at and past the 64-query tile), with no prior
+    context, a one-token prior and long priors, mixed with decodes in the same call."""
+    chunks = [(0, 2), (0, 64), (1, 63), (17, 65), (300, 130), (1000, 16), (15, 33)]
+    w = make_custom_mixed(30 + B, 4, B, chunks, [1, 16, 300, 1025], name=f"chunks_B{B}")
+    full_check(w)
+
+
+def test_chunk_tiles_peaked_scores():
+    w = make_custom_mixed(41, 3, 16, [(200, 100), (0, 70)], [50], name="chunks_peaked",
+                          q_scale=4.0)
+    full_check(w, "q_scale=4")
+
+
+def test_chunk_only_batch():
+    """Every sequence is a chunk (no decode units); the tile kernel alone writes the output."""
+    w = make_custom_mixed(42, 2, 16, [(64, 64), (5, 128), (0, 256)], [], name="chunks_only")
+    full_check(w)

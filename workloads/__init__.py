@@ -13,5 +13,6 @@ from .configs import (  # noqa: F401
     make_config,
     make_small,
     make_custom_decode,
+    make_custom_mixed,
     CONFIG_NAMES,
 )

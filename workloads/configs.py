@@ -338,6 +338,26 @@ def make_custom_decode(seed, dtype, num_heads, head_dim, block_size, lens, num_b
                             write_one=write_one, q_scale=q_scale)
 
 
+def make_custom_mixed(seed, num_heads, block_size, chunks, decode_lens, name="custom_mixed",
+                      q_scale=1.0):
+    """Chunks (prior tokens, new tokens) attending causally, plus single-token decodes, in one
+    batch (order shuffled); every new token is also appended this step."""
+    rng = np.random.default_rng(seed)
+    lens = [p + n for p, n in chunks] + list(decode_lens)
+    qlens = [n for _, n in chunks] + [1] * len(decode_lens)
+    order = rng.permutation(len(lens))
+    lens = np.asarray(lens, np.int32)[order]
+    qlens = np.asarray(qlens, np.int32)[order]
+    need = int(sum(_cdiv(int(L), block_size) for L in lens))
+    nb = max(need + 2, _cdiv(5 * need, 4))
+    bt = _tables_from_permutation(rng, lens, block_size, nb)
+    filled = _filled_from_tables(bt, lens - qlens, block_size, nb)
+    return Workload(name=name, seed=seed, dtype="f16", num_heads=num_heads, head_dim=128,
+                    block_size=block_size, num_blocks=nb, context_lens=lens, query_lens=qlens,
+                    write_lens=qlens.copy(), block_tables=bt, filled_before=filled,
+                    q_scale=q_scale)
+
+
 _MAKERS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 
