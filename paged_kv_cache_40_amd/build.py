@@ -31,6 +31,13 @@ HIPFLAGS = [
 ]
 
 
+# Per-source extra flags.  The tile kernel keeps its MFMA accumulators in VGPRs (the
+# accumulator-register form made the compiler copy all accumulators every step).
+EXTRA_FLAGS = {
+    "pa_tile.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -56,7 +63,8 @@ def build(verbose: bool = False) -> str:
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        list(ex.map(lambda so: _run([cc, *HIPFLAGS, "-c", so[0], "-o", so[1]], verbose),
+        list(ex.map(lambda so: _run([cc, *HIPFLAGS, *EXTRA_FLAGS.get(os.path.basename(so[0]), []),
+                                     "-c", so[0], "-o", so[1]], verbose),
                     zip(srcs, objs)))
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
