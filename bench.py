@@ -57,6 +57,40 @@ def measured_traffic(kv_bytes_unused=None):
     return rec.get("bytes_per_launch")
 
 
+# ------------------------------------------------------------ hbm ceiling --
+
+def hbm_stream_read_gbs(buf, reps: int = 5) -> float:
+    """Median read bandwidth of the streaming-read probe over `buf` (a device tensor), GB/s."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_40_amd.build import PROBE_LIB
+
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.pa_probe_stream_read.restype = ctypes.c_int
+    lib.pa_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                         ctypes.c_int32, ctypes.c_void_p]
+    nbytes = (buf.numel() * buf.element_size()) // 16 * 16
+    blocks = 256 * 32
+    out = torch.empty(blocks * 256, dtype=torch.int32, device=buf.device)
+    stream = torch.cuda.current_stream()
+    times = []
+    for i in range(reps + 1):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        rc = lib.pa_probe_stream_read(buf.data_ptr(), nbytes, out.data_ptr(), blocks,
+                                      stream.cuda_stream)
+        b.record(stream)
+        if rc != 0:
+            raise RuntimeError("HBM probe launch failed")
+        torch.cuda.synchronize()
+        if i:
+            times.append(a.elapsed_time(b))
+    return nbytes / (float(np.median(times)) * 1e-3) / 1e9
+
+
 # ---------------------------------------------------------------- cpu leg --
 
 def _cpu_worker(args):
@@ -126,6 +160,112 @@ def cpu_baseline(w, t, nseq: int, workers: int):
 
 # ---------------------------------------------------------------- gpu leg --
 
+def _timed(fn, steps: int, warmup: int):
+    import numpy as np
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    return wall_ms, float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+
+def bench_config(args) -> int:
+    """One of the other batches: its whole step (copy-on-write copies, slot writes, attention)."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_40_amd import api
+    from workloads import CONFIG_NAMES, make_config
+
+    w = make_config(args.config, seed=args.config if args.seed == 5 else args.seed)
+    t = w.device_tensors("cuda")
+    need = api.pa_decode_workspace_bytes(w.num_queries, w.num_heads, w.head_dim,
+                                         w.max_context_len)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(t["q"])
+
+    def step():
+        if w.copy_pairs is not None and len(w.copy_pairs):
+            api.pa_copy_blocks(t["k_pool"], t["v_pool"], t["copy_pairs"])
+        if w.num_writes:
+            api.pa_write_kv(t["k_pool"], t["v_pool"], t["k_new"], t["v_new"], t["block_tables"],
+                            t["context_lens"], t["write_start_loc"])
+        api.pa_decode(out, t["q"], t["k_pool"], t["v_pool"], t["block_tables"], t["context_lens"],
+                      t["q_start_loc"], max_context_len=w.max_context_len,
+                      max_query_len=w.max_query_len, workspace=ws)
+
+    wall_ms, ev_ms = _timed(step, args.steps, args.warmup)
+    kv = w.kv_bytes_read()
+    B = w.block_size
+    unique = w.unique_blocks_read() * 2 * B * w.num_heads * w.head_dim * w.elt_bytes
+    rec = {
+        "metric": METRIC, "value": round(kv / (wall_ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": CONFIG_NAMES[args.config], "num_seqs": w.num_seqs,
+                   "num_heads": w.num_heads, "head_dim": w.head_dim, "block_size": B,
+                   "num_blocks": w.num_blocks, "num_queries": w.num_queries,
+                   "num_writes": w.num_writes,
+                   "copy_pairs": 0 if w.copy_pairs is None else len(w.copy_pairs),
+                   "kv_bytes_logical": kv, "kv_bytes_unique_blocks": unique},
+        "event_ms_per_step": round(ev_ms, 4),
+        "pct_hbm_peak_logical": round(100 * kv / (wall_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "seq_heads_per_s": round(w.num_seqs * w.num_heads / (wall_ms * 1e-3), 1),
+    }
+    if w.max_query_len > 1:
+        qh = w.num_queries * w.num_heads
+        rec["query_heads_per_s"] = round(qh / (wall_ms * 1e-3), 1)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def sweep_batch(w, t, args) -> None:
+    """Decode latency vs batch size (first S sequences of the batch), with the batch's scattered
+    block tables and with identity tables (each sequence's blocks contiguous in the pool)."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_40_amd import api
+
+    B = w.block_size
+    nb = -(-w.context_lens.astype(np.int64) // B)
+    ident = np.full_like(w.block_tables, -1)
+    pos = 0
+    for s in range(w.num_seqs):
+        ident[s, :nb[s]] = np.arange(pos, pos + nb[s])
+        pos += nb[s]
+    tables = {"scattered": t["block_tables"], "identity": torch.from_numpy(ident).cuda()}
+    for S in (1, 8, 32, 64, 128, 256):
+        if S > w.num_seqs:
+            break
+        kv = int(2 * w.context_lens[:S].astype(np.int64).sum() * w.num_heads * w.head_dim *
+                 w.elt_bytes)
+        mcl = int(w.context_lens[:S].max())
+        need = api.pa_decode_workspace_bytes(S, w.num_heads, w.head_dim, mcl)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(t["q"][:S])
+        for name, bt in tables.items():
+            def dec(bt=bt):
+                api.pa_decode(out, t["q"][:S], t["k_pool"], t["v_pool"], bt[:S],
+                              t["context_lens"][:S], max_context_len=mcl, workspace=ws)
+            _, ms = _timed(dec, max(5, args.steps // 2), 3)
+            print(json.dumps({"sweep": "decode latency vs batch", "num_seqs": S, "table": name,
+                              "decode_ms": round(ms, 4), "kv_bytes": kv,
+                              "GBs": round(kv / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,6 +276,10 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-workers", type=int, default=0, help="0 = min(16, host cores)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (PMC byte calibration)")
+    ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5],
+                    help="batch to time (5 = the headline batch; 1-4 print their own line)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also print decode latency vs batch size, scattered vs identity tables")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -151,6 +295,8 @@ def main(argv=None) -> int:
 
     _lib.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.config != 5:
+        return bench_config(args)
     w = make_config(5, seed=args.seed)
     print(f"[bench] generating {w.name}: S={w.num_seqs} H={w.num_heads} NB={w.num_blocks}",
           file=sys.stderr, flush=True)
@@ -207,6 +353,10 @@ def main(argv=None) -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    if args.sweep:
+        sweep_batch(w, t, args)
+    hbm = hbm_stream_read_gbs(t["k_pool"])
+
     kv = w.kv_bytes_read()
     ms_per_step = wall * 1e3 / args.steps
     value = kv / (ms_per_step * 1e-3) / 1e9
@@ -247,6 +397,8 @@ def main(argv=None) -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            "measured_stream_read": round(hbm, 1),
+            "frac_of_measured": round(achieved / hbm, 4),
         },
         "cpu_baseline": cpu,
     }

@@ -2,7 +2,9 @@
 
 Usage: python -m paged_kv_cache_40_amd.build [-v]
 Each .hip file under csrc/ is compiled to an object in _build/ (in parallel),
-then linked into paged_kv_cache_40_amd/libpagedkv.so.
+then linked into paged_kv_cache_40_amd/libpagedkv.so.  The HBM streaming-read
+probe that bench.py uses for context (probe/hbm_probe.hip) becomes a separate
+libpa_probe.so.
 """
 
 from __future__ import annotations
@@ -19,6 +21,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
+PROBE_SRC = os.path.join(PKG, "probe", "hbm_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libpa_probe.so")
 ARCH = "gfx950"
 
 # Packed FP32 instructions are disabled: hand-written and compiler-formed
@@ -69,6 +73,10 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    # measurement aid used by bench.py (not part of the attention library)
+    tmp = PROBE_LIB + ".tmp"
+    _run([cc, *HIPFLAGS, "-shared", PROBE_SRC, "-o", tmp], verbose)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 
