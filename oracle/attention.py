@@ -13,6 +13,15 @@ slot (j-1) mod B, and the block table maps a logical block to a physical one.
 Here tokens are counted from 0, so token j is at table entry j // B, slot
 j % B: the same mapping.
 
+Variants [P1 sec. 10, limitations: sliding-window and ALiBi attention need the
+block indexing adapted; P3 "메모리 관리": sliding layers keep only a fixed
+window of the most recent tokens].  The pages name them without formulas; the
+plainest readings are used:
+  * sliding window W > 0: the query at position p sees keys p-W+1 .. p (the W
+    most recent tokens, itself included); W = 0 means no window;
+  * ALiBi: a per-head slope m_h adds m_h * (j - p) to the score of key j (a
+    penalty growing linearly with distance; 0 for the query's own token).
+
 Readings where the pages leave a step open:
   * the query of the token at 0-based position p attends to keys 0..p, itself
     included (the sums run up to j = i);
@@ -42,11 +51,13 @@ def gather_context(pool: np.ndarray, table_row: np.ndarray, length: int,
 
 
 def attend(q: np.ndarray, keys: np.ndarray, values: np.ndarray,
-           positions: np.ndarray) -> np.ndarray:
+           positions: np.ndarray, window: int = 0, alibi_slopes=None) -> np.ndarray:
     """Causal softmax attention in fp64.
 
     q: [n][H][d] queries; keys, values: [L][H][d] (token order);
-    positions: [n] 0-based token position of each query (query attends keys 0..p).
+    positions: [n] 0-based token position of each query (query attends keys 0..p,
+    or p-window+1..p with a window); alibi_slopes: optional [H] slopes, adding
+    slope * (j - p) to the score of key j.
     Returns [n][H][d].
     """
     q = np.asarray(q, dtype=np.float64)
@@ -55,10 +66,14 @@ def attend(q: np.ndarray, keys: np.ndarray, values: np.ndarray,
     d = q.shape[-1]
     out = np.empty(q.shape, dtype=np.float64)
     for r, p in enumerate(positions):
-        n_keys = int(p) + 1
-        k = keys[:n_keys]                                    # [n_keys][H][d]
-        v = values[:n_keys]
+        p = int(p)
+        lo = max(0, p - window + 1) if window > 0 else 0
+        k = keys[lo:p + 1]                                   # [n_keys][H][d]
+        v = values[lo:p + 1]
         x = np.einsum("hd,jhd->hj", q[r], k) / np.sqrt(d)    # [H][n_keys]
+        if alibi_slopes is not None:
+            dist = np.arange(lo, p + 1, dtype=np.float64) - p          # j - p
+            x = x + np.asarray(alibi_slopes, np.float64)[:, None] * dist[None, :]
         x = x - x.max(axis=1, keepdims=True)
         w = np.exp(x)
         a = w / w.sum(axis=1, keepdims=True)                 # A_rj
@@ -68,7 +83,7 @@ def attend(q: np.ndarray, keys: np.ndarray, values: np.ndarray,
 
 def paged_attention_seq(q_rows: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
                         table_row: np.ndarray, context_len: int, block_size: int,
-                        heads=None) -> np.ndarray:
+                        heads=None, window: int = 0, alibi_slopes=None) -> np.ndarray:
     """Attention for the n query rows of one sequence (the last n of its context_len tokens).
 
     heads: optional list of head indices to compute (others are skipped); the result
@@ -80,13 +95,15 @@ def paged_attention_seq(q_rows: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarr
     if heads is not None:
         heads = list(heads)
         keys, values, q_rows = keys[:, heads], values[:, heads], q_rows[:, heads]
+        if alibi_slopes is not None:
+            alibi_slopes = np.asarray(alibi_slopes)[heads]
     positions = np.arange(context_len - n, context_len)
-    return attend(q_rows, keys, values, positions)
+    return attend(q_rows, keys, values, positions, window, alibi_slopes)
 
 
 def paged_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
                     block_tables: np.ndarray, context_lens: np.ndarray, block_size: int,
-                    q_start_loc=None) -> np.ndarray:
+                    q_start_loc=None, window: int = 0, alibi_slopes=None) -> np.ndarray:
     """Attention for a whole batch.
 
     q: [T][H][d]; sequence s owns query rows q_start_loc[s] .. q_start_loc[s+1]-1
@@ -101,5 +118,6 @@ def paged_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
         L = int(context_lens[s])
         if not (1 <= b - a <= L):
             raise ValueError(f"sequence {s}: {b - a} queries for context length {L}")
-        out[a:b] = paged_attention_seq(q[a:b], k_pool, v_pool, block_tables[s], L, block_size)
+        out[a:b] = paged_attention_seq(q[a:b], k_pool, v_pool, block_tables[s], L, block_size,
+                                       window=window, alibi_slopes=alibi_slopes)
     return out

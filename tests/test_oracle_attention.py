@@ -289,7 +289,7 @@ def test_rejects_more_queries_than_context():
 _attend = oatt.attend
 _gather = oatt.gather_context
 
-def _mut_attend_scale_d(q, keys, values, positions):
+def _mut_attend_scale_d(q, keys, values, positions, window=0, alibi_slopes=None):
     q, keys, values = (np.asarray(a, np.float64) for a in (q, keys, values))
     d = q.shape[-1]
     out = np.empty(q.shape)
@@ -301,7 +301,7 @@ def _mut_attend_scale_d(q, keys, values, positions):
     return out
 
 
-def _mut_attend_excludes_self(q, keys, values, positions):
+def _mut_attend_excludes_self(q, keys, values, positions, window=0, alibi_slopes=None):
     q, keys, values = (np.asarray(a, np.float64) for a in (q, keys, values))
     d = q.shape[-1]
     out = np.empty(q.shape)
@@ -314,7 +314,7 @@ def _mut_attend_excludes_self(q, keys, values, positions):
     return out
 
 
-def _mut_attend_norm_over_heads(q, keys, values, positions):
+def _mut_attend_norm_over_heads(q, keys, values, positions, window=0, alibi_slopes=None):
     q, keys, values = (np.asarray(a, np.float64) for a in (q, keys, values))
     d = q.shape[-1]
     out = np.empty(q.shape)
@@ -326,8 +326,8 @@ def _mut_attend_norm_over_heads(q, keys, values, positions):
     return out
 
 
-def _mut_attend_keys_as_values(q, keys, values, positions):
-    return _attend(q, keys, keys, positions)                          # planted: swapped operand
+def _mut_attend_keys_as_values(q, keys, values, positions, window=0, alibi_slopes=None):
+    return _attend(q, keys, keys, positions, window, alibi_slopes)    # planted: swapped operand
 
 
 def _mut_gather_slot(pool, table_row, length, block_size):
@@ -344,7 +344,8 @@ def _mut_gather_entry(pool, table_row, length, block_size):
     return out
 
 
-def _mut_positions_shift(q_rows, k_pool, v_pool, table_row, context_len, block_size, heads=None):
+def _mut_positions_shift(q_rows, k_pool, v_pool, table_row, context_len, block_size, heads=None,
+                         window=0, alibi_slopes=None):
     n = q_rows.shape[0]
     keys = _gather(k_pool, table_row, context_len, block_size)
     values = _gather(v_pool, table_row, context_len, block_size)
