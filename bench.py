@@ -230,6 +230,62 @@ def bench_config(args) -> int:
     return 0
 
 
+def bench_variant(args) -> int:
+    """The large batch with a sliding window and/or ALiBi slopes (pa_decode_ext): write + decode
+    per step; bytes = K and V rows inside each sequence's window."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_40_amd import api
+    from workloads import make_config
+
+    w = make_config(5, seed=args.seed)
+    t = w.device_tensors("cuda")
+    H, D = w.num_heads, w.head_dim
+    W = args.window
+    slopes = None
+    if args.alibi:
+        slopes = torch.tensor(2.0 ** (-8.0 * (np.arange(H) + 1) / H), dtype=torch.float32,
+                              device="cuda")
+    need = api.pa_decode_workspace_bytes(w.num_queries, H, D, w.max_context_len)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(t["q"])
+    stream = torch.cuda.current_stream()
+
+    def write():
+        api.pa_write_kv(t["k_pool"], t["v_pool"], t["k_new"], t["v_new"], t["block_tables"],
+                        t["context_lens"], stream=stream)
+
+    def decode():
+        api.pa_decode_ext(out, t["q"], t["k_pool"], t["v_pool"], t["block_tables"],
+                          t["context_lens"], max_context_len=w.max_context_len, workspace=ws,
+                          sliding_window=W, alibi_slopes=slopes, stream=stream)
+
+    def step():
+        write()
+        decode()
+
+    wall_ms, _ = _timed(step, args.steps, args.warmup)
+    _, decode_ms = _timed(decode, args.steps, args.warmup)
+    L = w.context_lens.astype(np.int64)
+    seen = np.minimum(L, W) if W > 0 else L
+    kv = int(2 * seen.sum() * H * D * w.elt_bytes)
+    rec = {
+        "metric": METRIC, "value": round(kv / (wall_ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "large-batch decode + KV write (256 seqs x 40 heads, contexts "
+                               "1025..4097) with a sliding window and/or ALiBi",
+                   "sliding_window": W, "alibi": bool(args.alibi), "kv_bytes_in_window": kv},
+        "decode_ms": round(decode_ms, 4),
+        "decode_GBs": round(kv / (decode_ms * 1e-3) / 1e9, 1),
+        "pct_hbm_peak_decode": round(100 * kv / (decode_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def sweep_batch(w, t, args) -> None:
     """Decode latency vs batch size (first S sequences of the batch), with the batch's scattered
     block tables and with identity tables (each sequence's blocks contiguous in the pool)."""
@@ -280,6 +336,10 @@ def main(argv=None) -> int:
                     help="batch to time (5 = the headline batch; 1-4 print their own line)")
     ap.add_argument("--sweep", action="store_true",
                     help="also print decode latency vs batch size, scattered vs identity tables")
+    ap.add_argument("--window", type=int, default=0,
+                    help="time the large batch with this sliding window instead (own line)")
+    ap.add_argument("--alibi", action="store_true",
+                    help="time the large batch with ALiBi slopes instead (own line)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -297,6 +357,8 @@ def main(argv=None) -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.config != 5:
         return bench_config(args)
+    if args.window or args.alibi:
+        return bench_variant(args)
     w = make_config(5, seed=args.seed)
     print(f"[bench] generating {w.name}: S={w.num_seqs} H={w.num_heads} NB={w.num_blocks}",
           file=sys.stderr, flush=True)

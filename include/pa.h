@@ -61,7 +61,7 @@ typedef enum {
   PA_OK = 0,
   PA_ERR_NULL = -1,        /* a required pointer is NULL                       */
   PA_ERR_SHAPE = -2,       /* sizes out of range or inconsistent              */
-  PA_ERR_UNSUPPORTED = -3, /* dtype / head_dim / block_size not built         */
+  PA_ERR_UNSUPPORTED = -3, /* dtype / head_dim / block_size / variant not built */
   PA_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than required         */
   PA_ERR_LAUNCH = -5       /* the HIP runtime rejected a kernel launch        */
 } pa_status;
@@ -125,6 +125,32 @@ int pa_decode(void* out, const void* q,
               int32_t max_context_len, int32_t max_query_len,
               int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t dtype,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_ext — pa_decode with the two attention variants the block indexing
+ * has to accommodate (P1 sec. 10, limitations: sliding-window attention and
+ * ALiBi; P3 "메모리 관리": sliding layers keep a fixed window of the most
+ * recent tokens).  The pages give no formulas; the readings implemented:
+ *   sliding_window W > 0: the query at position p attends to tokens
+ *     p-W+1 .. p only (W = 0: no window).  Blocks that hold only older tokens
+ *     are never read.
+ *   alibi_slopes: device float [num_heads] or NULL; slope_h * (j - p) is added
+ *     to the score q.k_j / sqrt(head_dim) of token j (0 for the query itself,
+ *     more negative with distance).
+ * pa_decode(...) is pa_decode_ext(..., 0, NULL, stream).  Both variants are
+ * built for single-query sequences only: with max_query_len > 1, a nonzero
+ * window or non-NULL slopes return PA_ERR_UNSUPPORTED.  sliding_window < 0
+ * returns PA_ERR_SHAPE.  The workspace requirement is unchanged.
+ */
+int pa_decode_ext(void* out, const void* q,
+                  const void* k_pool, const void* v_pool, int64_t num_blocks,
+                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                  const int32_t* context_lens, const int32_t* q_start_loc,
+                  int32_t num_seqs, int32_t num_tokens,
+                  int32_t max_context_len, int32_t max_query_len,
+                  int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t dtype,
+                  void* workspace, size_t workspace_bytes,
+                  int32_t sliding_window, const float* alibi_slopes, void* stream);
 
 /*
  * pa_copy_blocks — copy-on-write block copies, batched: for every pair

@@ -24,6 +24,9 @@ SIGNATURES = {
     "pa_decode_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32]),
     "pa_decode": (_c_int, [_vp, _vp, _vp, _vp, _c_i64, _vp, _c_i32, _vp, _vp, _c_i32, _c_i32,
                            _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _c_size, _vp]),
+    "pa_decode_ext": (_c_int, [_vp, _vp, _vp, _vp, _c_i64, _vp, _c_i32, _vp, _vp, _c_i32, _c_i32,
+                               _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _c_size, _c_i32,
+                               _vp, _vp]),
     "pa_copy_blocks": (_c_int, [_vp, _vp, _c_i64, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                 _vp]),
     "pa_strerror": (ctypes.c_char_p, [_c_int]),

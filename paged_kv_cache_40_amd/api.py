@@ -93,6 +93,16 @@ def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, q_start_loc=No
     workspace: a uint8 GPU tensor of at least pa_decode_workspace_bytes(...) bytes
     (allocated here when omitted).
     """
+    return pa_decode_ext(out, q, k_pool, v_pool, block_tables, context_lens, q_start_loc,
+                         max_context_len, max_query_len, workspace, 0, None, stream)
+
+
+def pa_decode_ext(out, q, k_pool, v_pool, block_tables, context_lens, q_start_loc=None,
+                  max_context_len: Optional[int] = None, max_query_len: int = 1,
+                  workspace: Optional[torch.Tensor] = None, sliding_window: int = 0,
+                  alibi_slopes: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """pa_decode with a sliding window (0 = none) and optional per-head ALiBi slopes
+    (float32 GPU tensor [num_heads])."""
     nb, bs, h, d, dt = _check_pool(k_pool, v_pool)
     S = context_lens.shape[0]
     T = q.shape[0]
@@ -108,10 +118,15 @@ def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, q_start_loc=No
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = _lib.load().pa_decode(
+    if alibi_slopes is not None:
+        _require(alibi_slopes.dtype == torch.float32 and alibi_slopes.is_cuda and
+                 alibi_slopes.is_contiguous() and alibi_slopes.numel() == h,
+                 "alibi_slopes must be a contiguous float32 GPU tensor [num_heads]")
+    st = _lib.load().pa_decode_ext(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), nb, _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), _ptr(q_start_loc), S, T, int(max_context_len),
-        int(max_query_len), h, d, bs, dt, _ptr(workspace), ws_bytes, _stream(stream))
+        int(max_query_len), h, d, bs, dt, _ptr(workspace), ws_bytes, int(sliding_window),
+        _ptr(alibi_slopes), _stream(stream))
     _lib.check(st, "pa_decode")
     return out
 

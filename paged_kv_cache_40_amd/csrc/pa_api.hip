@@ -37,7 +37,7 @@ const char* pa_strerror(int status) {
     case PA_OK: return "success";
     case PA_ERR_NULL: return "a required pointer argument is NULL";
     case PA_ERR_SHAPE: return "sizes out of range or inconsistent";
-    case PA_ERR_UNSUPPORTED: return "dtype, head_dim or block_size not supported";
+    case PA_ERR_UNSUPPORTED: return "dtype, head_dim, block_size or variant not supported";
     case PA_ERR_WORKSPACE: return "workspace missing or smaller than pa_decode_workspace_bytes";
     case PA_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status";
@@ -87,7 +87,24 @@ int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
               int32_t num_tokens, int32_t max_context_len, int32_t max_query_len,
               int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t dtype,
               void* workspace, size_t workspace_bytes, void* stream) {
+  return pa_decode_ext(out, q, k_pool, v_pool, num_blocks, block_tables, max_blocks_per_seq,
+                       context_lens, q_start_loc, num_seqs, num_tokens, max_context_len,
+                       max_query_len, num_heads, head_dim, block_size, dtype, workspace,
+                       workspace_bytes, 0, nullptr, stream);
+}
+
+int pa_decode_ext(void* out, const void* q, const void* k_pool, const void* v_pool,
+                  int64_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                  const int32_t* context_lens, const int32_t* q_start_loc, int32_t num_seqs,
+                  int32_t num_tokens, int32_t max_context_len, int32_t max_query_len,
+                  int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t dtype,
+                  void* workspace, size_t workspace_bytes, int32_t sliding_window,
+                  const float* alibi_slopes, void* stream) {
   if (int st = check_layout(num_blocks, num_heads, head_dim, block_size, dtype)) return st;
+  if (sliding_window < 0) return PA_ERR_SHAPE;
+  // the multi-query tile path has no window / bias variant
+  if (max_query_len > 1 && (sliding_window > 0 || alibi_slopes != nullptr))
+    return PA_ERR_UNSUPPORTED;
   if (num_seqs <= 0 || num_tokens <= 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
   if (max_context_len <= 0 || max_query_len <= 0 || max_query_len > max_context_len)
     return PA_ERR_SHAPE;
@@ -121,6 +138,8 @@ int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
   a.block_size = block_size;
   a.max_context_len = max_context_len;
   a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(head_dim)));
+  a.window = sliding_window;
+  a.alibi = alibi_slopes;
   a.workspace = workspace;
   hipStream_t st = static_cast<hipStream_t>(stream);
   // single-query sequences: context partitions + merge; the kernels skip the others

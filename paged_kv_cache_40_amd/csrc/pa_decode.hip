@@ -138,14 +138,19 @@ void decode_partition_kernel(DecodeArgs a) {
   }
   if (qrow < 0 || qrow >= a.num_tokens) return;
   const int ctx = min(a.context_lens[s], min(a.max_blocks * BS, a.max_context_len));
-  const int nparts = (ctx + P - 1) / P;
+  // with a sliding window the query (position ctx-1) sees tokens lo .. ctx-1; partitions
+  // start at the window's first block, so older blocks are never read
+  const int lo = a.window > 0 ? max(0, ctx - a.window) : 0;
+  const int first = lo / BS * BS;
+  const int span = ctx - first;
+  const int nparts = (span + P - 1) / P;
 #if PA_DECODE_BALANCED
   // equal shares (rounded up to whole trips and blocks), so no partition is a short tail
-  const int share = ((ctx + nparts - 1) / nparts + C::kAlign - 1) / C::kAlign * C::kAlign;
+  const int share = ((span + nparts - 1) / nparts + C::kAlign - 1) / C::kAlign * C::kAlign;
 #else
   const int share = P;
 #endif
-  const int start = part * share;
+  const int start = first + part * share;
   if (start >= ctx) {
     // Rounded-up shares can leave a trailing partition without tokens; the merge pass
     // still reads it, so it records an empty partial (m = -inf, l = 0, acc = 0).
@@ -229,11 +234,14 @@ void decode_partition_kernel(DecodeArgs a) {
     }
   };
 
-  auto score = [&](const u32x4 (&kr)[C::kCpt]) {
+  // ALiBi: slope * (j - p) added to the score of token j, p = ctx - 1 (log2 units here)
+  const float slope = a.alibi != nullptr ? a.alibi[h] * kLog2e : 0.f;
+  auto score = [&](const u32x4 (&kr)[C::kCpt], int rel) {
     float d = 0.f;
 #pragma unroll
     for (int j = 0; j < C::kCpt; ++j) d = chunk_dot<T>(qc[j], kr[j], d);
-    return group_sum<8>(d) * a.scale_log2;
+    const float x = group_sum<8>(d) * a.scale_log2;
+    return fmaf(slope, static_cast<float>(start + rel - (ctx - 1)), x);
   };
 
   const int full = ntok / C::kTrip;
@@ -252,10 +260,23 @@ void decode_partition_kernel(DecodeArgs a) {
       for (int j = 0; j < C::kCpt; ++j) vr[i][j] = ld_kv(vbase + off[i] + col(j));
     float sc[C::kG];
     bool ok[C::kG];
+    // Only the trips that begin before the window's first token mask anything (the window's
+    // first block may start earlier); their masked value rows are cleared so whatever those
+    // slots hold gets weight exactly zero.
+    const bool head_trip = start + trip * C::kTrip < lo;  // wave-uniform
 #pragma unroll
     for (int i = 0; i < C::kG; ++i) {
-      sc[i] = score(kr[i]);
-      ok[i] = true;
+      const int rel = trip * C::kTrip + i * 8 + g;
+      ok[i] = start + rel >= lo;
+      const float x = score(kr[i], rel);
+      sc[i] = ok[i] ? x : -INFINITY;
+    }
+    if (head_trip) {
+#pragma unroll
+      for (int i = 0; i < C::kG; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kCpt; ++j)
+          if (!ok[i]) vr[i][j] = u32x4{0, 0, 0, 0};
     }
     update(sc, vr, ok);
   }
@@ -266,7 +287,7 @@ void decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < C::kG; ++i) {
       const int base = full * C::kTrip + i * 8;
-      ok[i] = base + g < ntok;
+      ok[i] = base + g < ntok && start + base + g >= lo;
 #pragma unroll
       for (int j = 0; j < C::kCpt; ++j) {
         kr[i][j] = u32x4{0, 0, 0, 0};
@@ -285,7 +306,7 @@ void decode_partition_kernel(DecodeArgs a) {
     float sc[C::kG];
 #pragma unroll
     for (int i = 0; i < C::kG; ++i) {
-      const float d = score(kr[i]);
+      const float d = score(kr[i], full * C::kTrip + i * 8 + g);
       sc[i] = ok[i] ? d : -INFINITY;
     }
     update(sc, vr, ok);
@@ -347,7 +368,9 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   }
   if (qrow < 0 || qrow >= a.num_tokens) return;
   const int ctx = min(a.context_lens[s], min(a.max_blocks * a.block_size, a.max_context_len));
-  const int nparts = min((ctx + a.part_size - 1) / a.part_size, a.num_parts_max);
+  const int lo = a.window > 0 ? max(0, ctx - a.window) : 0;
+  const int span = ctx - lo / a.block_size * a.block_size;
+  const int nparts = min((span + a.part_size - 1) / a.part_size, a.num_parts_max);
   if (nparts <= 1) return;  // pass 1 wrote the output
   const int64_t slot0 = (static_cast<int64_t>(qrow) * a.num_heads + h) * a.num_parts_max;
   const float* ml = a.ws_ml + slot0 * 2;
@@ -377,11 +400,18 @@ size_t decode_workspace_bytes(int64_t num_tokens, int64_t num_heads, int64_t hea
   return static_cast<size_t>(num_tokens * num_heads * nparts * (head_dim + 2) * 4);
 }
 
+// Longest token span one (sequence, head) reads: the context, or with a sliding window
+// the window plus the part of its first block that precedes it.
+static int decode_span(const DecodeArgs& a, int block_size, int max_context_len) {
+  if (a.window <= 0) return max_context_len;
+  return max_context_len < a.window + block_size - 1 ? max_context_len : a.window + block_size - 1;
+}
+
 template <typename T, int D, int BS, int P>
 static hipError_t launch_decode_t(const DecodeArgs& a0, int max_context_len, hipStream_t stream) {
   DecodeArgs a = a0;
   a.part_size = P;
-  const int nparts = (max_context_len + P - 1) / P;
+  const int nparts = (decode_span(a, BS, max_context_len) + P - 1) / P;
   a.num_parts_max = nparts;
   // ws_ml follows ws_acc; both fit the workspace sized for kMinPartition-token partitions
   a.ws_acc = static_cast<float*>(a.workspace);
@@ -419,7 +449,7 @@ static int pick_partition(const DecodeArgs& a, int block_size, int max_context_l
 
 template <typename T, int D, int BS>
 static hipError_t launch_decode_p(const DecodeArgs& a, int max_context_len, hipStream_t stream) {
-  const int p = pick_partition(a, BS, max_context_len);
+  const int p = pick_partition(a, BS, decode_span(a, BS, max_context_len));
   constexpr int kCapP = BS == 8 ? 1024 : 2048;
   switch (p < kCapP ? p : kCapP) {
     case 256: return launch_decode_t<T, D, BS, 256>(a, max_context_len, stream);

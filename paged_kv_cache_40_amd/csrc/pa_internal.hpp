@@ -23,6 +23,8 @@ struct DecodeArgs {
   int32_t block_size;
   int32_t max_context_len; // host bound; device context lengths are clamped to it
   float scale_log2;        // log2(e) / sqrt(head_dim)
+  int32_t window;          // sliding window in tokens (0 = none)
+  const float* alibi;      // per-head ALiBi slopes [num_heads] or nullptr
   void* workspace;         // caller's scratch (see decode_workspace_bytes)
   // set by the launcher:
   int32_t num_parts_max;   // partition slots per (query row, head) in the workspace

@@ -22,17 +22,27 @@ def log(msg: str) -> None:
     print(msg, flush=True)
 
 
-def run_library(w, t, stream=None, workspace=None):
-    """copy-on-write copies -> slot writes -> attention, in stream order. Returns out."""
+def run_library(w, t, stream=None, workspace=None, window=0, alibi=None):
+    """copy-on-write copies -> slot writes -> attention, in stream order. Returns out.
+
+    window / alibi (host float slopes [H]) select the pa_decode_ext variants."""
     if w.copy_pairs is not None and len(w.copy_pairs):
         api.pa_copy_blocks(t["k_pool"], t["v_pool"], t["copy_pairs"], stream=stream)
     if w.num_writes:
         api.pa_write_kv(t["k_pool"], t["v_pool"], t["k_new"], t["v_new"], t["block_tables"],
                         t["context_lens"], t["write_start_loc"], stream=stream)
     out = torch.empty_like(t["q"])
-    api.pa_decode(out, t["q"], t["k_pool"], t["v_pool"], t["block_tables"], t["context_lens"],
-                  t["q_start_loc"], max_context_len=w.max_context_len,
-                  max_query_len=w.max_query_len, workspace=workspace, stream=stream)
+    if window == 0 and alibi is None:
+        api.pa_decode(out, t["q"], t["k_pool"], t["v_pool"], t["block_tables"],
+                      t["context_lens"], t["q_start_loc"], max_context_len=w.max_context_len,
+                      max_query_len=w.max_query_len, workspace=workspace, stream=stream)
+    else:
+        slopes = None if alibi is None else torch.tensor(np.asarray(alibi, np.float32),
+                                                         device=t["q"].device)
+        api.pa_decode_ext(out, t["q"], t["k_pool"], t["v_pool"], t["block_tables"],
+                          t["context_lens"], t["q_start_loc"], max_context_len=w.max_context_len,
+                          max_query_len=w.max_query_len, workspace=workspace,
+                          sliding_window=window, alibi_slopes=slopes, stream=stream)
     return out
 
 
@@ -40,8 +50,10 @@ def host_copy(t: dict) -> dict:
     return {k: (None if v is None else v.cpu().numpy()) for k, v in t.items()}
 
 
-def oracle_step(w, h: dict):
-    """The oracle's copy -> write -> attention on host arrays. Returns (out, k_pool, v_pool)."""
+def oracle_step(w, h: dict, window=0, alibi=None):
+    """The oracle's copy -> write -> attention on host arrays. Returns (out, k_pool, v_pool).
+
+    alibi slopes are taken as the float32 values the library receives."""
     kp, vp = h["k_pool"], h["v_pool"]
     if w.copy_pairs is not None and len(w.copy_pairs):
         kp, vp = oracle.copy_blocks(kp, vp, h["copy_pairs"])
@@ -49,8 +61,13 @@ def oracle_step(w, h: dict):
         kp, vp = oracle.write_kv(kp, vp, h["k_new"], h["v_new"], h["block_tables"],
                                  h["context_lens"], w.block_size, h["write_start_loc"])
     out = oracle.paged_attention(h["q"], kp, vp, h["block_tables"], h["context_lens"],
-                                 w.block_size, h["q_start_loc"])
+                                 w.block_size, h["q_start_loc"], window=window,
+                                 alibi_slopes=_slopes64(alibi))
     return out, kp, vp
+
+
+def _slopes64(alibi):
+    return None if alibi is None else np.asarray(alibi, np.float32).astype(np.float64)
 
 
 def assert_close(gpu, ref, dtype: str, what: str = "") -> float:
@@ -138,7 +155,7 @@ def snapshot_for(w, t, seqs):
     return sub
 
 
-def oracle_sub(w, sub, heads=None):
+def oracle_sub(w, sub, heads=None, window=0, alibi=None):
     """Oracle copy -> write -> attention on a compact sub-problem.  Returns the per-sequence
     outputs of the sampled sequences and the compact pools without the scratch block."""
     kp, vp = sub["k_pool"], sub["v_pool"]
@@ -152,7 +169,8 @@ def oracle_sub(w, sub, heads=None):
     for i in range(sub["num_attn"]):
         outs.append(oracle.paged_attention_seq(sub["q"][qsl[i]:qsl[i + 1]], kp, vp,
                                                sub["block_tables"][i], int(sub["context_lens"][i]),
-                                               w.block_size, heads=heads))
+                                               w.block_size, heads=heads, window=window,
+                                               alibi_slopes=_slopes64(alibi)))
     return outs, kp[:-1], vp[:-1]
 
 

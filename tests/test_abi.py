@@ -78,6 +78,25 @@ def decode(lib, **kw):
                          a["dt"], a["ws"], a["wsb"], None)
 
 
+def decode_ext(lib, window=0, alibi=None, **kw):
+    a = dict(o=FAKE, q=FAKE, k=FAKE, v=FAKE, nb=64, bt=FAKE, mb=8, cl=FAKE, qsl=None, S=4, T=4,
+             mcl=100, mql=1, H=2, D=64, B=16, dt=0, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.pa_decode_ext(a["o"], a["q"], a["k"], a["v"], a["nb"], a["bt"], a["mb"], a["cl"],
+                             a["qsl"], a["S"], a["T"], a["mcl"], a["mql"], a["H"], a["D"], a["B"],
+                             a["dt"], a["ws"], a["wsb"], window, alibi, None)
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(window=-1), -2),
+    (dict(window=8, mql=2, qsl=FAKE, T=5, dt=1, D=128), -3),      # no multi-query variant
+    (dict(alibi=FAKE, mql=2, qsl=FAKE, T=5, dt=1, D=128), -3),
+    (dict(window=8, o=None), -1), (dict(alibi=FAKE, D=32), -3), (dict(window=8, mcl=129), -2),
+])
+def test_decode_ext_rejects(lib, args, code):
+    assert decode_ext(lib, **args) == code
+
+
 def copy_blocks(lib, **kw):
     a = dict(k=FAKE, v=FAKE, nb=64, pairs=FAKE, n=3, H=2, D=64, B=16, dt=1)
     a.update(kw)

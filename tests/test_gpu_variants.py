@@ -1,0 +1,164 @@
+"""GPU parity of the sliding-window and ALiBi variants (pa_decode_ext) vs the fp64 oracle.
+
+Readings under test (oracle/attention.py): with window W the query at position
+p attends to tokens p-W+1 .. p; ALiBi adds slope_h * (j - p) to the score of
+token j.  Slopes are the geometric sequence 2^(-8(h+1)/H) of the ALiBi paper;
+the pages name the method without values, and any positive slopes take the
+same code path.  Tolerances as in the plain tests (paged_harness.TOL).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_40_amd import api
+from workloads import make_config, make_custom_decode
+from paged_harness import (assert_bits_equal, assert_close, host_copy, log, oracle_step,
+                           oracle_sub, pick_sequences, run_library, snapshot_for)
+
+pytestmark = pytest.mark.gpu
+
+EDGE_LENS = [1, 2, 7, 8, 9, 15, 16, 17, 31, 32, 33, 255, 256, 257, 511, 512, 513, 1000, 2049]
+
+
+def geometric_slopes(H):
+    return (2.0 ** (-8.0 * (np.arange(H) + 1) / H)).astype(np.float32)
+
+
+def variant_check(w, window, alibi, note=""):
+    log(f"[case] {w.name} W={window} alibi={alibi is not None} S={w.num_seqs} "
+        f"H={w.num_heads} d={w.head_dim} B={w.block_size} {w.dtype} {note}")
+    t = w.device_tensors("cuda")
+    h = host_copy(t)
+    out = run_library(w, t, window=window, alibi=alibi)
+    torch.cuda.synchronize()
+    ref, kp, vp = oracle_step(w, h, window=window, alibi=alibi)
+    err = assert_close(out.cpu().numpy(), ref, w.dtype, f"{w.name} W={window}")
+    assert_bits_equal(t["k_pool"].cpu().numpy(), kp, "k_pool")
+    assert_bits_equal(t["v_pool"].cpu().numpy(), vp, "v_pool")
+    log(f"[ok] max abs err {err:.3g}")
+
+
+CASES = [(W, al) for W in (0, 1, 7, 16, 100, 300, 5000) for al in (False, True)
+         if W or al]
+
+
+@pytest.mark.parametrize("dtype,head_dim,block_size",
+                         [("f16", 128, 16), ("f32", 64, 8), ("f16", 64, 32), ("f32", 128, 32)])
+@pytest.mark.parametrize("window,use_alibi", CASES)
+def test_window_alibi_edge_lengths(dtype, head_dim, block_size, window, use_alibi):
+    """Windows shorter than a block, equal to one, spanning partitions and longer than every
+    context, with and without ALiBi, over context lengths at block and partition edges; the
+    step also appends one token per sequence."""
+    w = make_custom_decode(50 + block_size, dtype, 3, head_dim, block_size, EDGE_LENS,
+                           write_one=True, name=f"variant_{dtype}_d{head_dim}_B{block_size}")
+    variant_check(w, window, geometric_slopes(3) if use_alibi else None)
+
+
+def test_large_slopes_peaked():
+    """Slopes large enough that only the newest few tokens carry weight."""
+    w = make_custom_decode(61, "f16", 4, 128, 16, [3, 40, 600, 3000], name="alibi_steep")
+    variant_check(w, 0, np.asarray([8.0, 2.0, 0.5, 0.125], np.float32))
+
+
+def test_history_before_window_is_never_used():
+    """Every slot older than the window holds NaN and the table entries of blocks wholly
+    before the window are -1 (a sliding-window cache would have released them): the output
+    must stay finite and equal the oracle's, which reads only the window."""
+    H, D, B, W = 4, 128, 16, 100
+    lens = [1, 50, 100, 101, 117, 300, 1000, 2500]
+    w = make_custom_decode(62, "f16", H, D, B, lens, name="window_poisoned_history")
+    log(f"[case] {w.name} W={W}")
+    t = w.device_tensors("cuda")
+    bt = t["block_tables"].cpu().numpy()
+    blks, slots = [], []
+    for s, L in enumerate(lens):
+        lo = max(0, L - W)
+        j = np.arange(lo)
+        blks.append(bt[s, j // B])
+        slots.append(j % B)
+        bt[s, :lo // B] = -1
+    blks = torch.from_numpy(np.concatenate(blks).astype(np.int64)).cuda()
+    slots = torch.from_numpy(np.concatenate(slots).astype(np.int64)).cuda()
+    t["k_pool"][blks, slots] = float("nan")
+    t["v_pool"][blks, slots] = float("nan")
+    t["block_tables"] = torch.from_numpy(bt).cuda()
+    h = host_copy(t)
+    slopes = geometric_slopes(H)
+    out = run_library(w, t, window=W, alibi=slopes)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    ref, _, _ = oracle_step(w, h, window=W, alibi=slopes)
+    assert_close(out.cpu().numpy(), ref, "f16", "poisoned history")
+    log("[ok]")
+
+
+def test_neutral_variants_bit_identical_to_plain():
+    """A window at least as long as every context, and all-zero slopes, reproduce pa_decode's
+    output bit for bit (same partitions, and adding 0 * (j - p) is exact)."""
+    w = make_custom_decode(63, "f16", 8, 128, 16, [1, 17, 300, 2049, 4000, 6000], name="neutral")
+    log(f"[case] {w.name}")
+    t = w.device_tensors("cuda")
+    plain = run_library(w, t)
+    wide = run_library(w, t, window=int(w.context_lens.max()))
+    zero = run_library(w, t, alibi=np.zeros(8, np.float32))
+    torch.cuda.synchronize()
+    assert torch.equal(plain.view(torch.int16), wide.view(torch.int16))
+    assert torch.equal(plain.view(torch.int16), zero.view(torch.int16))
+    log("[ok]")
+
+
+# Windows long enough to span several context partitions of each size the launch picks.
+@pytest.mark.parametrize("S,H,lo,hi,W", [
+    (64, 40, 3000, 9000, 2500),    # 256-token partitions inside the window
+    (256, 40, 1025, 4097, 4000),   # 2048-token partitions; short contexts end before W
+    (256, 40, 1025, 4097, 1024),   # 1024-token partitions
+])
+def test_window_partitions_sampled(S, H, lo, hi, W):
+    rng = np.random.default_rng(S + W)
+    lens = rng.integers(lo, hi + 1, size=S)
+    lens[0], lens[-1] = lo, hi
+    w = make_custom_decode(64, "f16", H, 128, 16, lens, write_one=True,
+                           name=f"window_{W}_S{S}")
+    slopes = geometric_slopes(H)
+    log(f"[case] {w.name} L=[{lo},{hi}] W={W} NB={w.num_blocks}")
+    t = w.device_tensors("cuda")
+    seqs = pick_sequences(w, n=3, seed=S)
+    sub = snapshot_for(w, t, seqs)
+    out = run_library(w, t, window=W, alibi=slopes)
+    torch.cuda.synchronize()
+    refs, kp, _ = oracle_sub(w, sub, window=W, alibi=slopes)
+    for i, s in enumerate(seqs):
+        assert_close(out[s:s + 1].cpu().numpy(), refs[i], w.dtype, f"{w.name} seq {s}")
+    idx_t = torch.tensor(sub["uniq"], dtype=torch.int64, device="cuda")
+    assert_bits_equal(t["k_pool"].index_select(0, idx_t).cpu().numpy(), kp, "k_pool sampled")
+    log("[ok]")
+
+
+def test_full_size_large_batch_window_alibi_sampled():
+    """The 256-sequence, 40-head large-batch decode (contexts 1025..4097) with a 1024-token
+    window and ALiBi, as the benchmark's variant line runs it; sampled sequences, every head."""
+    w = make_config(5)
+    W = 1024
+    slopes = geometric_slopes(w.num_heads)
+    log(f"[case] full {w.name} W={W} alibi")
+    t = w.device_tensors("cuda")
+    seqs = pick_sequences(w, n=4, seed=9)
+    sub = snapshot_for(w, t, seqs)
+    out = run_library(w, t, window=W, alibi=slopes)
+    torch.cuda.synchronize()
+    refs, _, _ = oracle_sub(w, sub, window=W, alibi=slopes)
+    for i, s in enumerate(seqs):
+        assert_close(out[s:s + 1].cpu().numpy(), refs[i], w.dtype, f"{w.name} seq {s}")
+    log("[ok]")
+
+
+def test_multi_query_variant_rejected():
+    w = make_custom_decode(65, "f16", 2, 128, 16, [40, 50], name="reject")
+    t = w.device_tensors("cuda")
+    q = torch.zeros(3, 2, 128, dtype=torch.float16, device="cuda")
+    qsl = torch.tensor([0, 2, 3], dtype=torch.int32, device="cuda")
+    with pytest.raises(RuntimeError, match="variant"):
+        api.pa_decode_ext(torch.empty_like(q), q, t["k_pool"], t["v_pool"], t["block_tables"],
+                          t["context_lens"], qsl, max_context_len=50, max_query_len=2,
+                          sliding_window=16)

@@ -103,7 +103,7 @@ def _byte_sum_t(w):
     return (t & 0xFFFF) + (t >> 16)
 
 
-def normal_values_torch(seed: int, stream: int, out, offset: int = 0, chunk: int = 1 << 26):
+def normal_values_torch(seed: int, stream: int, out, offset: int = 0, chunk: int = 1 << 28):
     """Fill the contiguous torch tensor `out` (any float dtype, any device) in place.
 
     Element i of `out.view(-1)` receives the value for flat index offset + i, the
