@@ -10,8 +10,9 @@ What it computes (plain definitions, written out; no blocking, fusion or
 reordering beyond what the definitions state):
   * attention.py — softmax attention of each query over its sequence's keys,
     with the keys and values fetched token by token through the block table;
-  * kv_ops.py    — the slot write of newly generated tokens and the
-    copy-on-write whole-block copy;
+  * kv_ops.py    — the slot write of newly generated tokens, the
+    copy-on-write whole-block copy and the block swap between the device
+    pool and a host swap pool;
   * sizes.py     — the KV-cache byte formulas.
 
 Sources (cited by key in every file):
@@ -28,5 +29,5 @@ the figures the pages print); see tests/test_oracle_*.py.
 """
 
 from .attention import gather_context, attend, paged_attention, paged_attention_seq  # noqa: F401
-from .kv_ops import write_kv, copy_blocks  # noqa: F401
+from .kv_ops import write_kv, copy_blocks, swap_blocks  # noqa: F401
 from .sizes import kv_bytes_per_token, block_bytes  # noqa: F401

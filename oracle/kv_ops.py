@@ -9,6 +9,13 @@ entry (L-n+i) // B at slot (L-n+i) % B.
 copy_blocks [P2 pseudocode, copy_on_write; P1 sec. 6, Fig. 9]: the new block
 receives a copy of the whole shared block (every slot, filled or not), for
 K and for V.  All pairs read the pool as it was before any of them is applied.
+
+swap_blocks [P1 sec. 5, preemption: a sequence's KV blocks move to CPU memory
+and back; P3 "오프로딩": blocks are copied into a pre-allocated pinned CPU
+buffer in one batched transfer and copied back when the request resumes, with
+nothing recomputed]: block dst of the destination pool receives the whole
+block src of the source pool, K and V, unchanged.  Which pool lives on the
+host only decides the direction; the result is the same copy.
 """
 
 from __future__ import annotations
@@ -46,4 +53,16 @@ def copy_blocks(k_pool, v_pool, pairs):
     for src, dst in np.asarray(pairs).reshape(-1, 2):
         k_out[int(dst)] = k_pool[int(src)]
         v_out[int(dst)] = v_pool[int(src)]
+    return k_out, v_out
+
+
+def swap_blocks(dst_k, dst_v, src_k, src_v, pairs):
+    """Return new (dst_k, dst_v): destination block dst holds source block src, per (src, dst).
+
+    dst_* and src_* are two different pools of the same block layout (the device pool and a
+    host swap pool, either way round)."""
+    k_out, v_out = dst_k.copy(), dst_v.copy()
+    for src, dst in np.asarray(pairs).reshape(-1, 2):
+        k_out[int(dst)] = src_k[int(src)]
+        v_out[int(dst)] = src_v[int(src)]
     return k_out, v_out

@@ -17,10 +17,20 @@ Fig. 7-10):
     reference from the source; the last sharer left finds a count of one and
     writes in place).
 
+Swapping [P1 sec. 5: under memory pressure a preempted sequence's blocks move
+to CPU memory and come back later; P3 "오프로딩": one batched copy into a
+pre-allocated pinned CPU pool, copied back on resume]: a second, host pool
+has its own stack free list and counts.  swap_out moves a group of sequences
+(e.g. the samples of one request, which share blocks) to host blocks, one
+host block per distinct device block so sharing survives, and drops the
+group's device references; swap_in does the reverse.  Both are all or
+nothing: without room they raise MemoryError and change nothing.  Which
+request to swap, and when, is the scheduler's policy and not modelled here.
+
 The manager holds no K/V data.  It returns where each token goes and records
 the (src, dst) block pairs whose contents the device must copy; the device
 pools, the slot writes and the block copies are the library's
-pa_write_kv / pa_copy_blocks.
+pa_write_kv / pa_copy_blocks / pa_swap_blocks.
 """
 
 from __future__ import annotations
@@ -31,8 +41,8 @@ import numpy as np
 
 
 class BlockManager:
-    def __init__(self, num_blocks: int, block_size: int):
-        if num_blocks <= 0 or block_size <= 0:
+    def __init__(self, num_blocks: int, block_size: int, num_host_blocks: int = 0):
+        if num_blocks <= 0 or block_size <= 0 or num_host_blocks < 0:
             raise ValueError("num_blocks and block_size must be positive")
         self.num_blocks = int(num_blocks)
         self.block_size = int(block_size)
@@ -40,6 +50,10 @@ class BlockManager:
         self.ref_count = np.zeros(self.num_blocks, dtype=np.int64)
         self.num_filled = np.zeros(self.num_blocks, dtype=np.int64)
         self._copies: List[Tuple[int, int]] = []
+        self.num_host_blocks = int(num_host_blocks)
+        self.host_free: List[int] = list(range(self.num_host_blocks))
+        self.host_ref = np.zeros(self.num_host_blocks, dtype=np.int64)
+        self.host_filled = np.zeros(self.num_host_blocks, dtype=np.int64)
 
     # -- allocation ------------------------------------------------------
     def allocate_block(self) -> int:
@@ -111,6 +125,61 @@ class BlockManager:
         pairs = np.asarray(self._copies, dtype=np.int32).reshape(-1, 2)
         self._copies = []
         return pairs
+
+    # -- swapping --------------------------------------------------------
+    def swap_out(self, tables: Sequence[List[int]]) -> np.ndarray:
+        """Move the blocks of a group of sequences to the host pool.
+
+        Each table is rewritten in place with host block ids.  Returns the int32 [n][2]
+        (device src, host dst) pairs to copy, one per distinct device block, before any of
+        those device blocks is reused.
+        """
+        distinct = list(dict.fromkeys(int(b) for t in tables for b in t))
+        for b in distinct:
+            if self.ref_count[b] <= 0:
+                raise ValueError(f"block {b} is not allocated")
+        if len(distinct) > len(self.host_free):
+            raise MemoryError("no room in the host swap pool")
+        mapping = {}
+        for b in distinct:
+            h = self.host_free.pop()
+            mapping[b] = h
+            self.host_filled[h] = self.num_filled[b]
+        for t in tables:
+            for i, b in enumerate(t):
+                h = mapping[int(b)]
+                self.host_ref[h] += 1
+                self.free_block(int(b))
+                t[i] = h
+        return np.asarray([(b, mapping[b]) for b in distinct], np.int32).reshape(-1, 2)
+
+    def swap_in(self, tables: Sequence[List[int]]) -> np.ndarray:
+        """Bring a swapped-out group back into newly allocated device blocks.
+
+        Each table is rewritten in place with device block ids.  Returns the int32 [n][2]
+        (host src, device dst) pairs to copy before the group runs again.
+        """
+        distinct = list(dict.fromkeys(int(h) for t in tables for h in t))
+        for h in distinct:
+            if self.host_ref[h] <= 0:
+                raise ValueError(f"host block {h} is not in use")
+        if len(distinct) > len(self.free_blocks):
+            raise MemoryError("no free KV cache blocks for swap-in")
+        mapping = {}
+        for h in distinct:
+            b = self.allocate_block()
+            self.ref_count[b] = 0
+            self.num_filled[b] = self.host_filled[h]
+            mapping[h] = b
+        for t in tables:
+            for i, h in enumerate(t):
+                b = mapping[int(h)]
+                self.ref_count[b] += 1
+                self.host_ref[int(h)] -= 1
+                if self.host_ref[int(h)] == 0:
+                    self.host_free.append(int(h))
+                t[i] = b
+        return np.asarray([(h, mapping[h]) for h in distinct], np.int32).reshape(-1, 2)
 
     # -- reporting -------------------------------------------------------
     def num_tokens(self, table: Sequence[int]) -> int:

@@ -195,3 +195,88 @@ def test_tables_to_array_pads_with_minus_one():
     a = tables_to_array([[3, 1], [], [5]], width=4)
     assert a.dtype == np.int32 and a.shape == (3, 4)
     assert a.tolist() == [[3, 1, -1, -1], [-1, -1, -1, -1], [5, -1, -1, -1]]
+
+
+# ------------------------------------------------------------------ swapping --
+# [P1 sec. 5: a preempted sequence's blocks go to CPU memory and come back;
+#  P3 "오프로딩": one batched copy into a pinned CPU pool and back on resume]
+
+def _sampled_group(bm, prompt=10, samples=3, gen=(2, 5, 7)):
+    root = []
+    bm.append_slots(root, prompt)
+    group = [bm.fork(root) for _ in range(samples)]
+    bm.free_table(root)
+    for t, n in zip(group, gen):
+        bm.append_slots(t, n)
+    bm.take_copies()
+    return group
+
+
+def _sharing(tables):
+    """Which (sequence, entry) positions hold the same block: a structure independent of ids."""
+    first = {}
+    return [[first.setdefault(b, (s, i)) for i, b in enumerate(t)] for s, t in enumerate(tables)]
+
+
+def test_swap_out_and_in_preserves_group_structure():
+    bm = BlockManager(40, 4, num_host_blocks=16)
+    group = _sampled_group(bm)
+    tokens = [bm.num_tokens(t) for t in group]
+    shape = _sharing(group)
+    free0 = bm.num_free()
+    distinct = len({b for t in group for b in t})
+    dev_ids = [list(t) for t in group]
+    out = bm.swap_out(group)
+    assert out.shape == (distinct, 2) and out.dtype == np.int32
+    assert sorted(out[:, 0].tolist()) == sorted({b for t in dev_ids for b in t})
+    assert bm.num_free() == free0 + distinct                  # device blocks released
+    assert len(bm.host_free) == 16 - distinct
+    assert _sharing(group) == shape                            # host tables share alike
+    # every table entry maps through the pair list
+    m = dict(out.tolist())
+    assert [[m[b] for b in t] for t in dev_ids] == group
+    back = bm.swap_in(group)
+    assert back.shape == (distinct, 2)
+    assert len(bm.host_free) == 16 and bm.num_free() == free0
+    assert _sharing(group) == shape
+    assert [bm.num_tokens(t) for t in group] == tokens         # fill counts carried
+    # the group runs on: appending still copies-on-write only where blocks are shared
+    for t in group:
+        bm.append_slot(t)
+    for s in range(3):
+        for b in group[s]:
+            assert bm.ref_count[b] == sum(b in t for t in group)
+
+
+def test_swap_keeps_blocks_shared_outside_the_group():
+    bm = BlockManager(20, 4, num_host_blocks=8)
+    a = []
+    bm.append_slots(a, 6)
+    b = bm.fork(a)
+    out = bm.swap_out([b])
+    assert len(out) == 2
+    assert all(bm.ref_count[x] == 1 for x in a)                # `a` keeps its device blocks
+    assert bm.num_tokens(a) == 6
+
+
+def test_swap_without_room_changes_nothing():
+    bm = BlockManager(12, 4, num_host_blocks=2)
+    group = _sampled_group(bm, prompt=8, samples=2, gen=(1, 1))
+    snap = (list(map(list, group)), bm.ref_count.copy(), list(bm.free_blocks),
+            list(bm.host_free))
+    with pytest.raises(MemoryError):
+        bm.swap_out(group)                                     # 4 distinct blocks, 2 host slots
+    assert (list(map(list, group)), list(bm.free_blocks), list(bm.host_free)) == \
+        (snap[0], snap[2], snap[3])
+    assert np.array_equal(bm.ref_count, snap[1])
+    # swap-in without device room
+    bm2 = BlockManager(5, 4, num_host_blocks=8)
+    g = []
+    bm2.append_slots(g, 12)                                    # 3 blocks
+    bm2.swap_out([g])
+    hold = [bm2.allocate_block() for _ in range(3)]            # 2 device blocks left
+    with pytest.raises(MemoryError):
+        bm2.swap_in([g])
+    assert len(bm2.host_free) == 5 and bm2.num_free() == 2
+    bm2.free_block(hold[0])
+    assert len(bm2.swap_in([g])) == 3

@@ -6,7 +6,10 @@ the history into a pool that holds only the first L-n must give exactly the
 pool that holds all L [P2 "SOSP 2023論文解説: vLLM — PagedAttentionによる
 KVキャッシュメモリ管理の革新", pseudocode: append_token].
 copy_blocks is checked block by block [P2 pseudocode: copy_on_write copies the
-whole block].  Sizes are pinned to the figures the pages print
+whole block].  swap_blocks is checked by a preemption round trip: blocks moved
+to a host pool, their device blocks overwritten, moved back into other blocks
+and the tables rewritten must give bit-identical attention [P1 sec. 5:
+swapped blocks are restored; P3 "오프로딩": resumed without recomputation].  Sizes are pinned to the figures the pages print
 (tests/golden/kv_sizes.json) and to the byte size of real arrays.
 """
 
@@ -122,6 +125,92 @@ def test_copy_blocks_whole_block_and_snapshot():
     # no pairs: unchanged copy
     k4, v4 = oracle.copy_blocks(kp, vp, np.zeros((0, 2), np.int32))
     assert k4.tobytes() == kp.tobytes() and k4 is not kp
+
+
+# ------------------------------------------------------------------- swap --
+
+def test_swap_blocks_bytes_and_payloads():
+    rng = np.random.default_rng(4)
+    dev_k = rng.standard_normal((12, 4, 2, 3)).astype(np.float16)
+    dev_v = rng.standard_normal((12, 4, 2, 3)).astype(np.float16)
+    # a NaN with a payload: swapping moves bits, so the payload must survive
+    dev_k.view(np.uint16)[3, 1, 0, 0] = 0x7E5A
+    host_k = np.full((12, 4, 2, 3), np.nan, np.float16)
+    host_v = np.full((12, 4, 2, 3), np.nan, np.float16)
+    pairs = np.asarray([[3, 0], [7, 4], [11, 5]], np.int32)
+    hk, hv = oracle.swap_blocks(host_k, host_v, dev_k, dev_v, pairs)
+    for src, dst in pairs:
+        assert hk[dst].tobytes() == dev_k[src].tobytes()
+        assert hv[dst].tobytes() == dev_v[src].tobytes()
+    assert hk.view(np.uint16)[0, 1, 0, 0] == 0x7E5A
+    for b in (1, 2, 3):
+        assert hk[b].tobytes() == host_k[b].tobytes()
+    # the source pool is only read; no pairs: an unchanged copy
+    assert hk is not host_k
+    e_k, e_v = oracle.swap_blocks(dev_k, dev_v, hk, hv, np.zeros((0, 2), np.int32))
+    assert e_k.tobytes() == dev_k.tobytes() and e_v.tobytes() == dev_v.tobytes()
+
+
+def test_swap_round_trip_restores_attention():
+    rng = np.random.default_rng(5)
+    B = 4
+    lens, _, NB, bt, kh, vh = make_case(rng, B=B, lens=(3, 9, 16, 17), wlens=(1, 1, 1, 1))
+    NB += 10                                                   # room to swap back elsewhere
+    kp = scatter(kh, lens, B, NB, bt)
+    vp = scatter(vh, lens, B, NB, bt)
+    q = rng.standard_normal((4, 2, 4))
+    before = oracle.paged_attention(q, kp, vp, bt, np.asarray(lens), B)
+    # swap sequences 1 and 3 out to a host pool
+    out_seqs = [1, 3]
+    blocks = [int(b) for s in out_seqs for b in bt[s] if b >= 0]
+    host_ids = rng.permutation(len(blocks) + 2)[:len(blocks)]
+    hk = np.full((len(blocks) + 2,) + kp.shape[1:], np.nan, np.float32)
+    hv = hk.copy()
+    hk, hv = oracle.swap_blocks(hk, hv, kp, vp, np.stack([blocks, host_ids], 1))
+    # their device blocks are reused by others meanwhile
+    kp[blocks] = rng.standard_normal(kp[blocks].shape)
+    vp[blocks] = rng.standard_normal(vp[blocks].shape)
+    # swap back into blocks nobody holds, and rewrite the two tables
+    used = {int(b) for b in bt.reshape(-1) if b >= 0}
+    free = [b for b in rng.permutation(NB) if int(b) not in used][:len(blocks)]
+    kp, vp = oracle.swap_blocks(kp, vp, hk, hv, np.stack([host_ids, free], 1))
+    bt2 = bt.copy()
+    it = iter(free)
+    for s in out_seqs:
+        for i, b in enumerate(bt2[s]):
+            if b >= 0:
+                bt2[s, i] = next(it)
+    after = oracle.paged_attention(q, kp, vp, bt2, np.asarray(lens), B)
+    assert np.array_equal(before, after)
+
+
+def _mut_swap_kv_crossed(dst_k, dst_v, src_k, src_v, pairs):
+    k_out, v_out = dst_k.copy(), dst_v.copy()
+    for src, dst in np.asarray(pairs).reshape(-1, 2):
+        k_out[int(dst)] = src_v[int(src)]                       # planted: K and V crossed
+        v_out[int(dst)] = src_k[int(src)]
+    return k_out, v_out
+
+
+_swap = kv_ops.swap_blocks
+
+
+def _mut_swap_pair_reversed(dst_k, dst_v, src_k, src_v, pairs):
+    return _swap(dst_k, dst_v, src_k, src_v, np.asarray(pairs).reshape(-1, 2)[:, ::-1])
+
+
+@pytest.mark.parametrize("mutant", [_mut_swap_kv_crossed, _mut_swap_pair_reversed])
+def test_swap_pins_catch_planted_mistake(monkeypatch, mutant):
+    monkeypatch.setattr(oracle, "swap_blocks", mutant)
+    caught = 0
+    for pin in (test_swap_blocks_bytes_and_payloads, test_swap_round_trip_restores_attention):
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+        except IndexError:          # a reversed pair may also leave the pool; not counted
+            pass
+    assert caught >= 1
 
 
 # ------------------------------------------------------------------ sizes --
