@@ -286,6 +286,74 @@ def bench_variant(args) -> int:
     return 0
 
 
+def bench_swap(args) -> int:
+    """Swap the K/V blocks of the first --swap-seqs sequences of the large batch out to a pinned
+    host pool and back (pa_swap_blocks), against plain contiguous copies of the same byte count
+    between device memory and pinned host memory (the host-link ceiling on this machine)."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_40_amd import api
+    from workloads import make_config
+
+    w = make_config(5, seed=args.seed)
+    t = w.device_tensors("cuda")
+    B = w.block_size
+    n = min(args.swap_seqs, w.num_seqs)
+    nb = -(-w.context_lens[:n].astype(np.int64) // B)
+    blocks = np.concatenate([w.block_tables[s, :nb[s]] for s in range(n)]).astype(np.int32)
+    NH = len(blocks)
+    shape = (NH,) + tuple(t["k_pool"].shape[1:])
+    hk = torch.empty(shape, dtype=torch.float16, pin_memory=True)
+    hv = torch.empty(shape, dtype=torch.float16, pin_memory=True)
+    host_ids = np.arange(NH, dtype=np.int32)
+    out_pairs = torch.from_numpy(np.stack([blocks, host_ids], 1)).cuda()
+    in_pairs = torch.from_numpy(np.stack([host_ids, blocks], 1)).cuda()
+    stream = torch.cuda.current_stream()
+    nbytes = 2 * NH * hk[0].numel() * hk.element_size()
+
+    def swap_out():
+        api.pa_swap_blocks(t["k_pool"], t["v_pool"], hk, hv, out_pairs, "out", stream=stream)
+
+    def swap_in():
+        api.pa_swap_blocks(t["k_pool"], t["v_pool"], hk, hv, in_pairs, "in", stream=stream)
+
+    dev_buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    host_buf = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+
+    def d2h():
+        host_buf.copy_(dev_buf, non_blocking=True)
+
+    def h2d():
+        dev_buf.copy_(host_buf, non_blocking=True)
+
+    steps = max(3, args.steps // 3)
+    res = {}
+    for name, fn in (("swap_out", swap_out), ("swap_in", swap_in), ("copy_d2h", d2h),
+                     ("copy_h2d", h2d)):
+        _, ms = _timed(fn, steps, 2)
+        res[name] = ms
+    gbs = {k: nbytes / (v * 1e-3) / 1e9 for k, v in res.items()}
+    value = 2 * nbytes / ((res["swap_out"] + res["swap_in"]) * 1e-3) / 1e9
+    rec = {
+        "metric": "KV block swap GB/s, device pool <-> pinned host pool (out + in)",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": 2,
+        "ms_per_step": round(res["swap_out"] + res["swap_in"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"swap out and back in every K/V block of {n} sequences of the "
+                               "large batch (256 x 40 heads, d=128, B=16, contexts 1025..4097)",
+                   "blocks": NH, "bytes_each_way": nbytes},
+        "swap_out_ms": round(res["swap_out"], 4), "swap_in_ms": round(res["swap_in"], 4),
+        "swap_out_GBs": round(gbs["swap_out"], 2), "swap_in_GBs": round(gbs["swap_in"], 2),
+        "contiguous_copy_d2h_GBs": round(gbs["copy_d2h"], 2),
+        "contiguous_copy_h2d_GBs": round(gbs["copy_h2d"], 2),
+        "frac_of_contiguous": {"out": round(gbs["swap_out"] / gbs["copy_d2h"], 4),
+                               "in": round(gbs["swap_in"] / gbs["copy_h2d"], 4)},
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def sweep_batch(w, t, args) -> None:
     """Decode latency vs batch size (first S sequences of the batch), with the batch's scattered
     block tables and with identity tables (each sequence's blocks contiguous in the pool)."""
@@ -340,6 +408,9 @@ def main(argv=None) -> int:
                     help="time the large batch with this sliding window instead (own line)")
     ap.add_argument("--alibi", action="store_true",
                     help="time the large batch with ALiBi slopes instead (own line)")
+    ap.add_argument("--swap", action="store_true",
+                    help="time pa_swap_blocks out and in against plain host-link copies (own line)")
+    ap.add_argument("--swap-seqs", type=int, default=64)
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -359,6 +430,8 @@ def main(argv=None) -> int:
         return bench_config(args)
     if args.window or args.alibi:
         return bench_variant(args)
+    if args.swap:
+        return bench_swap(args)
     w = make_config(5, seed=args.seed)
     print(f"[bench] generating {w.name}: S={w.num_seqs} H={w.num_heads} NB={w.num_blocks}",
           file=sys.stderr, flush=True)

@@ -9,7 +9,8 @@
  *   P3 = "연속 배치 처리 아키텍처" (Transformers docs, continuous batching architecture)
  *
  * Conventions shared by every entry point
- *   - Every pointer except the names given as host values is DEVICE memory,
+ *   - Every pointer except the names given as host values (and pa_swap_blocks'
+ *     host pool) is DEVICE memory,
  *     owned by the caller; the library keeps no pointer after returning, keeps
  *     no state between calls and allocates nothing.  Calls are thread-safe.
  *   - Tensors are dense, row-major, contiguous.
@@ -63,8 +64,11 @@ typedef enum {
   PA_ERR_SHAPE = -2,       /* sizes out of range or inconsistent              */
   PA_ERR_UNSUPPORTED = -3, /* dtype / head_dim / block_size / variant not built */
   PA_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than required         */
-  PA_ERR_LAUNCH = -5       /* the HIP runtime rejected a kernel launch        */
+  PA_ERR_LAUNCH = -5,      /* the HIP runtime rejected a kernel launch        */
+  PA_ERR_HOST_MEMORY = -6  /* host pool not pinned memory mapped for the device */
 } pa_status;
+
+typedef enum { PA_SWAP_OUT = 0, PA_SWAP_IN = 1 } pa_swap_direction;
 
 /*
  * pa_write_kv — store this step's new K/V rows into their cache slots.
@@ -162,6 +166,35 @@ int pa_decode_ext(void* out, const void* q,
  */
 int pa_copy_blocks(void* k_pool, void* v_pool, int64_t num_blocks,
                    const int32_t* block_pairs, int32_t num_pairs,
+                   int32_t num_heads, int32_t head_dim, int32_t block_size,
+                   int32_t dtype, void* stream);
+
+/*
+ * pa_swap_blocks — move whole blocks between the device pools and a host swap
+ * pool, all pairs in one launch (P1 sec. 5: under memory pressure a preempted
+ * sequence's KV blocks are swapped to CPU memory and restored later; P3
+ * "오프로딩": offloaded requests' blocks are copied into a pre-allocated pinned
+ * CPU buffer in one batched transfer and copied back on resume, nothing
+ * recomputed).
+ *   dev_k, dev_v: the device pools, num_dev_blocks blocks each (layout above).
+ *   host_k, host_v: HOST pointers to the swap pool, num_host_blocks blocks of
+ *     the same layout each, in pinned host memory mapped for the device
+ *     (hipHostMalloc, or torch tensors made with pin_memory=True).  Pageable
+ *     or registered-elsewhere memory returns PA_ERR_HOST_MEMORY; this is the
+ *     one check that queries the HIP runtime (no device work).
+ *   block_pairs: int32 [num_pairs][2] (src, dst), DEVICE memory.
+ *   direction PA_SWAP_OUT: host[dst] = dev[src] (K and V);
+ *             PA_SWAP_IN:  dev[dst] = host[src].
+ * Whole blocks are copied bit-exact, every slot filled or not.  Destinations
+ * must be distinct.  num_pairs == 0 is a no-op.  The copy is ordered on
+ * `stream` like every other call: a swap-out must be enqueued before anything
+ * that overwrites its source blocks, and the host may read the swap pool only
+ * after the stream has been synchronised.  Pairs outside either pool are
+ * skipped by the kernel.
+ */
+int pa_swap_blocks(void* dev_k, void* dev_v, int64_t num_dev_blocks,
+                   void* host_k, void* host_v, int64_t num_host_blocks,
+                   const int32_t* block_pairs, int32_t num_pairs, int32_t direction,
                    int32_t num_heads, int32_t head_dim, int32_t block_size,
                    int32_t dtype, void* stream);
 

@@ -13,7 +13,7 @@ from .block_manager import BlockManager, tables_to_array  # noqa: F401
 
 def __getattr__(name):
     if name in ("pa_write_kv", "pa_decode", "pa_decode_ext", "pa_copy_blocks",
-                "pa_decode_workspace_bytes", "pa_strerror"):
+                "pa_swap_blocks", "pa_decode_workspace_bytes", "pa_strerror"):
         from . import api
         return getattr(api, name)
     raise AttributeError(name)

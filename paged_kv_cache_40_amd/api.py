@@ -84,6 +84,31 @@ def pa_copy_blocks(k_pool, v_pool, block_pairs, stream=None) -> None:
     _lib.check(st, "pa_copy_blocks")
 
 
+def pa_swap_blocks(k_pool, v_pool, host_k, host_v, block_pairs, direction: str,
+                   stream=None) -> None:
+    """Move whole blocks between the device pools and a pinned host swap pool.
+
+    direction "out": host[dst] = device[src]; "in": device[dst] = host[src], per row
+    (src, dst) of block_pairs (int32 GPU tensor [n][2]).  host_k / host_v: CPU tensors of the
+    pool layout allocated with pin_memory=True."""
+    nb, bs, h, d, dt = _check_pool(k_pool, v_pool)
+    _check_index(block_pairs, "block_pairs")
+    _require(block_pairs.dim() == 2 and block_pairs.shape[1] == 2, "block_pairs must be [n][2]")
+    _require(direction in ("out", "in"), "direction must be 'out' or 'in'")
+    _require(host_k.dim() == 4 and host_k.shape == host_v.shape and
+             tuple(host_k.shape[1:]) == (bs, h, d), "host pools must be [n][block_size][H][d]")
+    _require(host_k.dtype == host_v.dtype == k_pool.dtype, "host pool dtype must match")
+    _require(not host_k.is_cuda and not host_v.is_cuda and host_k.is_contiguous() and
+             host_v.is_contiguous(), "host pools must be contiguous CPU tensors")
+    _require(host_k.is_pinned() and host_v.is_pinned(), "host pools must be pinned memory")
+    st = _lib.load().pa_swap_blocks(
+        _ptr(k_pool), _ptr(v_pool), nb, _ptr(host_k), _ptr(host_v), host_k.shape[0],
+        _ptr(block_pairs), block_pairs.shape[0],
+        _lib.PA_SWAP_OUT if direction == "out" else _lib.PA_SWAP_IN, h, d, bs, dt,
+        _stream(stream))
+    _lib.check(st, "pa_swap_blocks")
+
+
 def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, q_start_loc=None,
               max_context_len: Optional[int] = None, max_query_len: int = 1,
               workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:

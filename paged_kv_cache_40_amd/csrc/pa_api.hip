@@ -1,6 +1,7 @@
 // C ABI of the paged KV-cache library: host-side argument checks, then the
-// launchers.  Every check here runs before any HIP call, so a rejected call
-// touches neither the device nor the stream.
+// launchers.  Every check here runs before any launch, so a rejected call
+// touches neither the device nor the stream; only pa_swap_blocks asks the HIP
+// runtime (a query, no device work) whether its host pool is mapped memory.
 
 #include <math.h>
 
@@ -28,6 +29,24 @@ int check_layout(int64_t num_blocks, int32_t num_heads, int32_t head_dim, int32_
 
 int launch_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
 
+// Device address of a host range [p, p + bytes): both ends must lie in pinned host memory
+// mapped for the device, at the same distance apart as on the host; else nullptr.
+void* mapped_host_range(void* p, int64_t bytes) {
+  void* d0 = nullptr;
+  void* d1 = nullptr;
+  if (hipHostGetDevicePointer(&d0, p, 0) != hipSuccess || d0 == nullptr) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  char* last = static_cast<char*>(p) + (bytes - 1);
+  if (hipHostGetDevicePointer(&d1, last, 0) != hipSuccess || d1 == nullptr) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (static_cast<char*>(d1) - static_cast<char*>(d0) != bytes - 1) return nullptr;
+  return d0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -40,6 +59,7 @@ const char* pa_strerror(int status) {
     case PA_ERR_UNSUPPORTED: return "dtype, head_dim, block_size or variant not supported";
     case PA_ERR_WORKSPACE: return "workspace missing or smaller than pa_decode_workspace_bytes";
     case PA_ERR_LAUNCH: return "kernel launch failed";
+    case PA_ERR_HOST_MEMORY: return "host pool is not pinned host memory mapped for the device";
     default: return "unknown status";
   }
 }
@@ -79,6 +99,31 @@ int pa_copy_blocks(void* k_pool, void* v_pool, int64_t num_blocks, const int32_t
       static_cast<int64_t>(block_size) * num_heads * head_dim * elt_bytes(dtype);
   return launch_status(pa::launch_copy_blocks(k_pool, v_pool, num_blocks, block_pairs, num_pairs,
                                               block_bytes, static_cast<hipStream_t>(stream)));
+}
+
+int pa_swap_blocks(void* dev_k, void* dev_v, int64_t num_dev_blocks, void* host_k,
+                   void* host_v, int64_t num_host_blocks, const int32_t* block_pairs,
+                   int32_t num_pairs, int32_t direction, int32_t num_heads, int32_t head_dim,
+                   int32_t block_size, int32_t dtype, void* stream) {
+  if (int st = check_layout(num_dev_blocks, num_heads, head_dim, block_size, dtype)) return st;
+  if (num_host_blocks <= 0 || num_pairs < 0) return PA_ERR_SHAPE;
+  if (direction != PA_SWAP_OUT && direction != PA_SWAP_IN) return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (!dev_k || !dev_v || !host_k || !host_v || !block_pairs) return PA_ERR_NULL;
+  const int64_t block_bytes =
+      static_cast<int64_t>(block_size) * num_heads * head_dim * elt_bytes(dtype);
+  if (num_host_blocks > INT64_MAX / block_bytes) return PA_ERR_SHAPE;
+  void* hk = mapped_host_range(host_k, num_host_blocks * block_bytes);
+  void* hv = mapped_host_range(host_v, num_host_blocks * block_bytes);
+  if (hk == nullptr || hv == nullptr) return PA_ERR_HOST_MEMORY;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (direction == PA_SWAP_OUT)
+    return launch_status(pa::launch_swap_blocks(hk, hv, num_host_blocks, dev_k, dev_v,
+                                                num_dev_blocks, block_pairs, num_pairs,
+                                                block_bytes, s));
+  return launch_status(pa::launch_swap_blocks(dev_k, dev_v, num_dev_blocks, hk, hv,
+                                              num_host_blocks, block_pairs, num_pairs,
+                                              block_bytes, s));
 }
 
 int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,

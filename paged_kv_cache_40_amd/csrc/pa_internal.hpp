@@ -67,6 +67,9 @@ hipError_t launch_write_kv(void* k_pool, void* v_pool, int64_t num_blocks, const
                            const int32_t* context_lens, const int32_t* write_start_loc,
                            int32_t num_seqs, int32_t num_tokens, int64_t row_bytes,
                            int32_t block_size, hipStream_t stream);
+hipError_t launch_swap_blocks(void* dst_k, void* dst_v, int64_t dst_blocks, const void* src_k,
+                              const void* src_v, int64_t src_blocks, const int32_t* block_pairs,
+                              int32_t num_pairs, int64_t block_bytes, hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_pool, void* v_pool, int64_t num_blocks,
                               const int32_t* block_pairs, int32_t num_pairs, int64_t block_bytes,
                               hipStream_t stream);

@@ -13,7 +13,12 @@
 // copy_blocks [P2 pseudocode, copy_on_write; P1 sec. 6, Fig. 9]: a physical
 //   block is one contiguous B*H*d run of the pool; each workgroup copies a
 //   16 KB slice of one (pair, K-or-V) block with 16-byte accesses.
-// Both copies are bit-exact: bytes are moved, never converted.  Slots or
+// swap_blocks [P1 sec. 5, preemption by swapping; P3 "오프로딩"]: whole
+//   blocks between the device pool and a host swap pool in pinned memory that
+//   the device addresses directly, all pairs in one launch: the host link is
+//   driven by the loads and stores of many workgroups at once, each thread
+//   keeping four 16-byte transfers in flight.
+// All copies are bit-exact: bytes are moved, never converted.  Slots or
 // blocks that fall outside the pool (malformed device data) are skipped.
 
 #include "pa_common.hpp"
@@ -72,6 +77,50 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
   if (n <= 0) return;
   copy_row(pool + static_cast<int64_t>(dst) * block_bytes + lo,
            pool + static_cast<int64_t>(src) * block_bytes + lo, n);
+}
+
+// 16 KB slice per workgroup of 256 threads: four 16-byte loads in flight per thread
+// before the stores (a host-link access takes microseconds).
+__device__ __forceinline__ void copy_slice_4(char* dst, const char* src, int64_t bytes) {
+  constexpr int64_t kStep = kCopyThreads * 16;
+  int64_t off = static_cast<int64_t>(threadIdx.x) * 16;
+  for (; off + 3 * kStep < bytes; off += 4 * kStep) {
+    u32x4 r[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) r[u] = ld16(src + off + u * kStep);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) st16(dst + off + u * kStep, r[u]);
+  }
+  for (; off < bytes; off += kStep) st16(dst + off, ld16(src + off));
+}
+
+__global__ __launch_bounds__(kCopyThreads) void swap_blocks_kernel(
+    char* dst_k, char* dst_v, int64_t dst_blocks, const char* src_k, const char* src_v,
+    int64_t src_blocks, const int32_t* block_pairs, int64_t block_bytes) {
+  const int pr = blockIdx.x;
+  const int src = block_pairs[2 * pr];
+  const int dst = block_pairs[2 * pr + 1];
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const int64_t lo = static_cast<int64_t>(blockIdx.y) * kCopySlice;
+  const int64_t n = min(kCopySlice, block_bytes - lo);
+  if (n <= 0) return;
+  const int64_t so = static_cast<int64_t>(src) * block_bytes + lo;
+  const int64_t d_o = static_cast<int64_t>(dst) * block_bytes + lo;
+  if (blockIdx.z == 0)
+    copy_slice_4(dst_k + d_o, src_k + so, n);
+  else
+    copy_slice_4(dst_v + d_o, src_v + so, n);
+}
+
+hipError_t launch_swap_blocks(void* dst_k, void* dst_v, int64_t dst_blocks, const void* src_k,
+                              const void* src_v, int64_t src_blocks, const int32_t* block_pairs,
+                              int32_t num_pairs, int64_t block_bytes, hipStream_t stream) {
+  dim3 grid(num_pairs, static_cast<unsigned>((block_bytes + kCopySlice - 1) / kCopySlice), 2);
+  hipLaunchKernelGGL(swap_blocks_kernel, grid, dim3(kCopyThreads), 0, stream,
+                     static_cast<char*>(dst_k), static_cast<char*>(dst_v), dst_blocks,
+                     static_cast<const char*>(src_k), static_cast<const char*>(src_v), src_blocks,
+                     block_pairs, block_bytes);
+  return hipGetLastError();
 }
 
 hipError_t launch_write_kv(void* k_pool, void* v_pool, int64_t num_blocks, const void* k_new,

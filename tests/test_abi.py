@@ -29,8 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("pa_write_kv", "pa_decode", "pa_copy_blocks", "pa_decode_workspace_bytes",
-              "pa_strerror"):
+    for n in ("pa_write_kv", "pa_decode", "pa_decode_ext", "pa_copy_blocks", "pa_swap_blocks",
+              "pa_decode_workspace_bytes", "pa_strerror"):
         assert n in names
 
 
@@ -135,6 +135,32 @@ def test_decode_rejects(lib, kw, code):
 ])
 def test_copy_blocks_rejects(lib, kw, code):
     assert copy_blocks(lib, **kw) == code
+
+
+def swap_blocks(lib, **kw):
+    a = dict(dk=FAKE, dv=FAKE, nb=64, hk=FAKE, hv=FAKE, nh=32, pairs=FAKE, n=3, dir=0, H=2, D=64,
+             B=16, dt=1)
+    a.update(kw)
+    return lib.pa_swap_blocks(a["dk"], a["dv"], a["nb"], a["hk"], a["hv"], a["nh"], a["pairs"],
+                              a["n"], a["dir"], a["H"], a["D"], a["B"], a["dt"], None)
+
+
+# every case fails before the host-memory query, so no HIP call is made
+@pytest.mark.parametrize("kw,code", [
+    (dict(dk=None), -1), (dict(hv=None), -1), (dict(pairs=None), -1),
+    (dict(nh=0), -2), (dict(n=-1), -2), (dict(dir=2), -2), (dict(dir=-1), -2), (dict(nb=0), -2),
+    (dict(D=96), -3), (dict(dt=3), -3),
+])
+def test_swap_blocks_rejects(lib, kw, code):
+    assert swap_blocks(lib, **kw) == code
+
+
+def test_swap_blocks_zero_pairs_is_a_noop(lib):
+    assert swap_blocks(lib, n=0, pairs=None, hk=None) == 0
+
+
+def test_strerror_host_memory(lib):
+    assert b"pinned" in lib.pa_strerror(-6)
 
 
 def test_copy_blocks_zero_pairs_is_a_noop(lib):
