@@ -354,6 +354,106 @@ def bench_swap(args) -> int:
     return 0
 
 
+def bench_beam(args) -> int:
+    """Beam-search decoding on the large-batch shape: 64 requests (prompts U{1024..4096}) x width
+    --beam candidates, 40 heads, d=128, B=16, fp16.  The block manager's steps (forks, prunes,
+    copy-on-write pairs, slots, tables) are computed on the host first; the timed loop runs each
+    step's pa_copy_blocks + pa_write_kv + pa_decode on the GPU."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_40_amd import BlockManager, api, tables_to_array
+    from paged_kv_cache_40_amd.beam import BeamSearchKV, memory_saving
+    from workloads.beam import beam_rows_torch, make_beam_tree
+
+    W, H, D, B, R, steps = args.beam, 40, 128, 16, 64, args.beam_steps
+    rng = np.random.default_rng(args.seed)
+    prompts = rng.integers(1024, 4097, size=R)
+    trees = [make_beam_tree(1000 + i, W, steps, int(P)) for i, P in enumerate(prompts)]
+    NB = int(sum(W * (-(-(int(P) + steps) // B) + 1) for P in prompts))
+    bm = BlockManager(NB, B)
+    reqs = [BeamSearchKV(bm, tr.prompt_len) for tr in trees]
+    prefill_tables = tables_to_array([r.beams[0] for r in reqs])
+    plan, savings = [], []
+    host_s = 0.0
+    for t in range(steps):
+        t0 = time.perf_counter()
+        for r, tr in zip(reqs, trees):
+            r.step(tr.parents[t])
+        pairs = bm.take_copies()
+        tables = [tb for r in reqs for tb in r.beams]
+        lens = np.asarray([n for r in reqs for n in r.num_tokens()], np.int32)
+        plan.append((pairs, tables_to_array(tables), lens))
+        host_s += time.perf_counter() - t0
+        savings.append(memory_saving(reqs))
+    host_ms = host_s * 1e3 / steps
+    print(f"[bench] beam plan: {steps} steps, host bookkeeping {host_ms:.2f} ms/step",
+          file=sys.stderr, flush=True)
+
+    kp = torch.empty((NB, B, H, D), dtype=torch.float16, device="cuda")
+    vp = torch.empty_like(kp)
+    gen = [beam_rows_torch(tr, H, D, torch.float16, "cuda") for tr in trees]
+    wsl = torch.tensor(np.concatenate([[0], np.cumsum(prompts)]), dtype=torch.int32, device="cuda")
+    api.pa_write_kv(kp, vp, torch.cat([g[0][:int(P)] for g, P in zip(gen, prompts)]),
+                    torch.cat([g[1][:int(P)] for g, P in zip(gen, prompts)]),
+                    torch.from_numpy(prefill_tables).cuda(),
+                    torch.tensor(prompts, dtype=torch.int32, device="cuda"), wsl)
+    dev = []
+    for t, (pairs, bt, lens) in enumerate(plan):
+        ids = [tr.token_id(t, b) for tr in trees for b in range(W)]
+        req = [i for i in range(R) for _ in range(W)]
+        kn = torch.stack([gen[i][0][j] for i, j in zip(req, ids)])
+        vn = torch.stack([gen[i][1][j] for i, j in zip(req, ids)])
+        q = torch.cat([g[2][t] for g in gen])
+        dev.append(dict(pairs=torch.from_numpy(pairs).cuda() if len(pairs) else None,
+                        bt=torch.from_numpy(bt).cuda(), cl=torch.from_numpy(lens).cuda(),
+                        mcl=int(lens.max()), kn=kn, vn=vn, q=q))
+    del gen
+    mcl = max(d["mcl"] for d in dev)
+    ws = torch.empty(max(api.pa_decode_workspace_bytes(R * W, H, D, mcl), 1), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((R * W, H, D), dtype=torch.float16, device="cuda")
+    torch.cuda.synchronize()
+
+    def run_step(d):
+        if d["pairs"] is not None:
+            api.pa_copy_blocks(kp, vp, d["pairs"])
+        api.pa_write_kv(kp, vp, d["kn"], d["vn"], d["bt"], d["cl"])
+        api.pa_decode(out, d["q"], kp, vp, d["bt"], d["cl"], max_context_len=d["mcl"],
+                      workspace=ws)
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    t0 = time.perf_counter()
+    for d in dev:
+        run_step(d)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ev_ms = ev0.elapsed_time(ev1) / steps
+    logical = int(sum(2 * int(lens.astype(np.int64).sum()) * H * D * 2 for _, _, lens in plan))
+    unique = int(sum(2 * held * B * H * D * 2 for held, _, _ in savings))
+    copies = int(sum(len(p) for p, _, _ in plan))
+    rec = {
+        "metric": "beam-search decode step: K/V GB/s read (logical) and candidate tokens/s",
+        "value": round(logical / steps / (ev_ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": steps, "warmup": 0, "ms_per_step": round(ev_ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"beam search, 64 requests x width {W}, prompts U{{1024..4096}}, "
+                               "40 heads, d=128, B=16, fp16, synthetic beam trees",
+                   "width": W, "requests": R, "num_blocks": NB},
+        "wall_ms_per_step": round(wall_ms, 4),
+        "candidate_tokens_per_s": round(R * W / (ev_ms * 1e-3), 1),
+        "unique_block_GBs": round(unique / steps / (ev_ms * 1e-3) / 1e9, 2),
+        "cow_copies_per_step": round(copies / steps, 2),
+        "memory_saving_mean": round(float(np.mean([s for _, _, s in savings])), 4),
+        "memory_saving_final": round(savings[-1][2], 4),
+        "host_bookkeeping_ms_per_step": round(host_ms, 3),
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def sweep_batch(w, t, args) -> None:
     """Decode latency vs batch size (first S sequences of the batch), with the batch's scattered
     block tables and with identity tables (each sequence's blocks contiguous in the pool)."""
@@ -411,6 +511,9 @@ def main(argv=None) -> int:
     ap.add_argument("--swap", action="store_true",
                     help="time pa_swap_blocks out and in against plain host-link copies (own line)")
     ap.add_argument("--swap-seqs", type=int, default=64)
+    ap.add_argument("--beam", type=int, default=0,
+                    help="time beam-search decoding with this beam width instead (own line)")
+    ap.add_argument("--beam-steps", type=int, default=64)
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -432,6 +535,8 @@ def main(argv=None) -> int:
         return bench_variant(args)
     if args.swap:
         return bench_swap(args)
+    if args.beam:
+        return bench_beam(args)
     w = make_config(5, seed=args.seed)
     print(f"[bench] generating {w.name}: S={w.num_seqs} H={w.num_heads} NB={w.num_blocks}",
           file=sys.stderr, flush=True)
