@@ -454,6 +454,110 @@ def bench_beam(args) -> int:
     return 0
 
 
+def bench_prefix(args) -> int:
+    """Shared-prefix prefill with the content-hash prefix cache: 64 requests = a --prefix-token
+    shared prefix + a private suffix of U{16..128} tokens, 40 heads, d=128, B=16, fp16.
+    Cold: every prompt token is written and attended (chunked-prefill tile path).  Warm: the
+    prefix blocks come from the cache (one earlier request computed them), only the suffix is
+    written and attended, over the whole context."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_40_amd import api, tables_to_array
+    from paged_kv_cache_40_amd.prefix_cache import PrefixCachingAllocator
+    from workloads.gen import normal_values_torch
+
+    H, D, B, R, P = 40, 128, 16, 64, args.prefix
+    rng = np.random.default_rng(args.seed)
+    suffix = rng.integers(16, 129, size=R)
+    prefix_tokens = list(range(P))
+    prompts = [prefix_tokens + [10**6 + r * 1000 + j for j in range(int(n))]
+               for r, n in enumerate(suffix)]
+    lens = np.asarray([len(p) for p in prompts], np.int32)
+    NB = int(sum(-(-int(L) // B) for L in lens)) + 64
+
+    def rows(stream, n):
+        t = torch.empty((n, H, D), dtype=torch.float16, device="cuda")
+        normal_values_torch(args.seed, stream, t)
+        return t
+
+    pk, pv, pq = rows(31, P), rows(32, P), rows(33, P)
+    sk, sv, sq = rows(34, int(suffix.sum())), rows(35, int(suffix.sum())), rows(36, int(suffix.sum()))
+    soff = np.concatenate([[0], np.cumsum(suffix)])
+
+    def prompt_rows(src_p, src_s, r, start):
+        """Rows of prompt r from token `start` on."""
+        parts = []
+        if start < P:
+            parts.append(src_p[start:])
+        parts.append(src_s[int(soff[r]) + max(0, start - P):int(soff[r + 1])])
+        return torch.cat(parts)
+
+    def plan(alloc, warm):
+        if warm:                                  # one earlier request computed the prefix
+            t, _ = alloc.allocate(prefix_tokens + [0])
+            alloc.commit(t, prefix_tokens + [0])
+        tables, cached = [], []
+        for p in prompts:
+            t, c = alloc.allocate(p)
+            tables.append(t)
+            cached.append(c)
+        nq = lens - np.asarray(cached, np.int32)
+        loc = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+        kn = torch.cat([prompt_rows(pk, sk, r, c) for r, c in enumerate(cached)])
+        vn = torch.cat([prompt_rows(pv, sv, r, c) for r, c in enumerate(cached)])
+        q = torch.cat([prompt_rows(pq, sq, r, c) for r, c in enumerate(cached)])
+        held = len({b for t in tables for b in t})
+        return dict(bt=torch.from_numpy(tables_to_array(tables)).cuda(),
+                    cl=torch.from_numpy(lens).cuda(), ql=torch.from_numpy(loc).cuda(),
+                    kn=kn, vn=vn, q=q, out=torch.empty_like(q), mql=int(nq.max()),
+                    queries=int(nq.sum()), cached=int(sum(cached)), held=held,
+                    hits=alloc.hits, lookups=alloc.lookups)
+
+    res = {}
+    for name, warm in (("cold", False), ("warm", True)):
+        alloc = PrefixCachingAllocator(NB, B)
+        kp = torch.zeros((NB, B, H, D), dtype=torch.float16, device="cuda")
+        vp = torch.zeros_like(kp)
+        d = plan(alloc, warm)
+        if warm:
+            first = d["bt"][0, :P // B].long()
+            kp[first] = pk[:P // B * B].view(-1, B, H, D)      # the cached prefix blocks
+            vp[first] = pv[:P // B * B].view(-1, B, H, D)
+        ws = torch.empty(max(api.pa_decode_workspace_bytes(d["queries"], H, D, int(lens.max())), 1),
+                         dtype=torch.uint8, device="cuda")
+
+        def step(d=d, kp=kp, vp=vp, ws=ws):
+            api.pa_write_kv(kp, vp, d["kn"], d["vn"], d["bt"], d["cl"], d["ql"])
+            api.pa_decode(d["out"], d["q"], kp, vp, d["bt"], d["cl"], d["ql"],
+                          max_context_len=int(lens.max()), max_query_len=d["mql"], workspace=ws)
+
+        _, ms = _timed(step, args.steps, args.warmup)
+        res[name] = dict(ms=ms, d=d)
+        del kp, vp
+    warm = res["warm"]["d"]
+    unshared = int(sum(-(-int(L) // B) for L in lens))
+    rec = {
+        "metric": "shared-prefix prefill: ms per batch, cold vs prefix-cached",
+        "value": round(res["warm"]["ms"], 4), "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(res["warm"]["ms"], 4),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"64 requests = {P}-token shared prefix + U{{16..128}}-token "
+                               "suffix, 40 heads, d=128, B=16, fp16; content-hash prefix cache",
+                   "prefix": P, "requests": R, "prompt_tokens": int(lens.sum())},
+        "cold_ms": round(res["cold"]["ms"], 4), "warm_ms": round(res["warm"]["ms"], 4),
+        "speedup": round(res["cold"]["ms"] / res["warm"]["ms"], 3),
+        "queries_cold": res["cold"]["d"]["queries"], "queries_warm": warm["queries"],
+        "cached_tokens": warm["cached"],
+        "block_hit_rate": round(warm["hits"] / warm["lookups"], 4) if warm["lookups"] else 0.0,
+        "blocks_held_warm": warm["held"], "blocks_unshared": unshared,
+        "blocks_saved": round(1 - warm["held"] / unshared, 4),
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def sweep_batch(w, t, args) -> None:
     """Decode latency vs batch size (first S sequences of the batch), with the batch's scattered
     block tables and with identity tables (each sequence's blocks contiguous in the pool)."""
@@ -514,6 +618,8 @@ def main(argv=None) -> int:
     ap.add_argument("--beam", type=int, default=0,
                     help="time beam-search decoding with this beam width instead (own line)")
     ap.add_argument("--beam-steps", type=int, default=64)
+    ap.add_argument("--prefix", type=int, default=0,
+                    help="time shared-prefix prefill, cold vs prefix-cached (own line)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -537,6 +643,8 @@ def main(argv=None) -> int:
         return bench_swap(args)
     if args.beam:
         return bench_beam(args)
+    if args.prefix:
+        return bench_prefix(args)
     w = make_config(5, seed=args.seed)
     print(f"[bench] generating {w.name}: S={w.num_seqs} H={w.num_heads} NB={w.num_blocks}",
           file=sys.stderr, flush=True)
