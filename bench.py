@@ -193,6 +193,7 @@ def bench_config(args) -> int:
                                          w.max_context_len)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(t["q"])
+    shared = w.shares_blocks() and not args.no_shared_hint
 
     def step():
         if w.copy_pairs is not None and len(w.copy_pairs):
@@ -200,9 +201,9 @@ def bench_config(args) -> int:
         if w.num_writes:
             api.pa_write_kv(t["k_pool"], t["v_pool"], t["k_new"], t["v_new"], t["block_tables"],
                             t["context_lens"], t["write_start_loc"])
-        api.pa_decode(out, t["q"], t["k_pool"], t["v_pool"], t["block_tables"], t["context_lens"],
-                      t["q_start_loc"], max_context_len=w.max_context_len,
-                      max_query_len=w.max_query_len, workspace=ws)
+        api.pa_decode_ext(out, t["q"], t["k_pool"], t["v_pool"], t["block_tables"],
+                          t["context_lens"], t["q_start_loc"], max_context_len=w.max_context_len,
+                          max_query_len=w.max_query_len, workspace=ws, shared_blocks=shared)
 
     wall_ms, ev_ms = _timed(step, args.steps, args.warmup)
     kv = w.kv_bytes_read()
@@ -218,6 +219,7 @@ def bench_config(args) -> int:
                    "num_blocks": w.num_blocks, "num_queries": w.num_queries,
                    "num_writes": w.num_writes,
                    "copy_pairs": 0 if w.copy_pairs is None else len(w.copy_pairs),
+                   "shared_blocks_hint": shared,
                    "kv_bytes_logical": kv, "kv_bytes_unique_blocks": unique},
         "event_ms_per_step": round(ev_ms, 4),
         "pct_hbm_peak_logical": round(100 * kv / (wall_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
@@ -419,8 +421,8 @@ def bench_beam(args) -> int:
         if d["pairs"] is not None:
             api.pa_copy_blocks(kp, vp, d["pairs"])
         api.pa_write_kv(kp, vp, d["kn"], d["vn"], d["bt"], d["cl"])
-        api.pa_decode(out, d["q"], kp, vp, d["bt"], d["cl"], max_context_len=d["mcl"],
-                      workspace=ws)
+        api.pa_decode_ext(out, d["q"], kp, vp, d["bt"], d["cl"], max_context_len=d["mcl"],
+                          workspace=ws, shared_blocks=not args.no_shared_hint)
 
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
@@ -441,7 +443,8 @@ def bench_beam(args) -> int:
         "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": f"beam search, 64 requests x width {W}, prompts U{{1024..4096}}, "
                                "40 heads, d=128, B=16, fp16, synthetic beam trees",
-                   "width": W, "requests": R, "num_blocks": NB},
+                   "width": W, "requests": R, "num_blocks": NB,
+                   "shared_blocks_hint": not args.no_shared_hint},
         "wall_ms_per_step": round(wall_ms, 4),
         "candidate_tokens_per_s": round(R * W / (ev_ms * 1e-3), 1),
         "unique_block_GBs": round(unique / steps / (ev_ms * 1e-3) / 1e9, 2),
@@ -618,6 +621,8 @@ def main(argv=None) -> int:
     ap.add_argument("--beam", type=int, default=0,
                     help="time beam-search decoding with this beam width instead (own line)")
     ap.add_argument("--beam-steps", type=int, default=64)
+    ap.add_argument("--no-shared-hint", action="store_true",
+                    help="never pass the shared-blocks hint (for comparison)")
     ap.add_argument("--prefix", type=int, default=0,
                     help="time shared-prefix prefill, cold vs prefix-cached (own line)")
     args = ap.parse_args(argv)

@@ -70,6 +70,9 @@ typedef enum {
 
 typedef enum { PA_SWAP_OUT = 0, PA_SWAP_IN = 1 } pa_swap_direction;
 
+/* pa_decode_ext flags */
+typedef enum { PA_DECODE_SHARED_BLOCKS = 1 } pa_decode_flags;
+
 /*
  * pa_write_kv — store this step's new K/V rows into their cache slots.
  * Defined by the append step of the block manager (P2, pseudocode section:
@@ -141,10 +144,21 @@ int pa_decode(void* out, const void* q,
  *   alibi_slopes: device float [num_heads] or NULL; slope_h * (j - p) is added
  *     to the score q.k_j / sqrt(head_dim) of token j (0 for the query itself,
  *     more negative with distance).
- * pa_decode(...) is pa_decode_ext(..., 0, NULL, stream).  Both variants are
- * built for single-query sequences only: with max_query_len > 1, a nonzero
- * window or non-NULL slopes return PA_ERR_UNSUPPORTED.  sliding_window < 0
- * returns PA_ERR_SHAPE.  The workspace requirement is unchanged.
+ * flags: 0, or PA_DECODE_SHARED_BLOCKS when neighbouring sequences of the
+ *   batch share blocks (the samples of one prompt, the beams of one search,
+ *   requests with a cached common prefix, placed next to each other): the
+ *   single-query kernels then keep K/V rows cached and run neighbouring
+ *   sequences on the same die, so shared blocks are fetched from HBM about
+ *   once (P1 sec. 6: shared blocks are what parallel sampling, beam search
+ *   and shared prefixes save).  Results are bit-identical either way; only
+ *   speed differs.  Unknown bits return PA_ERR_UNSUPPORTED; with the flag,
+ *   num_heads * num_seqs * ceil(max_context_len / 256) must stay below 2^24
+ *   (PA_ERR_SHAPE).
+ * pa_decode(...) is pa_decode_ext(..., 0, NULL, 0, stream).  The window and
+ * ALiBi variants are built for single-query sequences only: with
+ * max_query_len > 1, a nonzero window or non-NULL slopes return
+ * PA_ERR_UNSUPPORTED.  sliding_window < 0 returns PA_ERR_SHAPE.  The
+ * workspace requirement is unchanged.
  */
 int pa_decode_ext(void* out, const void* q,
                   const void* k_pool, const void* v_pool, int64_t num_blocks,
@@ -154,7 +168,8 @@ int pa_decode_ext(void* out, const void* q,
                   int32_t max_context_len, int32_t max_query_len,
                   int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t dtype,
                   void* workspace, size_t workspace_bytes,
-                  int32_t sliding_window, const float* alibi_slopes, void* stream);
+                  int32_t sliding_window, const float* alibi_slopes, uint32_t flags,
+                  void* stream);
 
 /*
  * pa_copy_blocks — copy-on-write block copies, batched: for every pair

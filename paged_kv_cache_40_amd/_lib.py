@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.
 PA_F32, PA_F16 = 0, 1
 PA_OK = 0
 PA_SWAP_OUT, PA_SWAP_IN = 0, 1
+PA_DECODE_SHARED_BLOCKS = 1
 
 _c_int, _c_i32, _c_i64, _c_size = ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 _vp = ctypes.c_void_p
@@ -27,7 +28,7 @@ SIGNATURES = {
                            _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _c_size, _vp]),
     "pa_decode_ext": (_c_int, [_vp, _vp, _vp, _vp, _c_i64, _vp, _c_i32, _vp, _vp, _c_i32, _c_i32,
                                _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _c_size, _c_i32,
-                               _vp, _vp]),
+                               _vp, ctypes.c_uint32, _vp]),
     "pa_copy_blocks": (_c_int, [_vp, _vp, _c_i64, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                 _vp]),
     "pa_swap_blocks": (_c_int, [_vp, _vp, _c_i64, _vp, _vp, _c_i64, _vp, _c_i32, _c_i32, _c_i32,

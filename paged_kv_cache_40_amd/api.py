@@ -119,15 +119,17 @@ def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, q_start_loc=No
     (allocated here when omitted).
     """
     return pa_decode_ext(out, q, k_pool, v_pool, block_tables, context_lens, q_start_loc,
-                         max_context_len, max_query_len, workspace, 0, None, stream)
+                         max_context_len, max_query_len, workspace, 0, None, False, stream)
 
 
 def pa_decode_ext(out, q, k_pool, v_pool, block_tables, context_lens, q_start_loc=None,
                   max_context_len: Optional[int] = None, max_query_len: int = 1,
                   workspace: Optional[torch.Tensor] = None, sliding_window: int = 0,
-                  alibi_slopes: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """pa_decode with a sliding window (0 = none) and optional per-head ALiBi slopes
-    (float32 GPU tensor [num_heads])."""
+                  alibi_slopes: Optional[torch.Tensor] = None, shared_blocks: bool = False,
+                  stream=None) -> torch.Tensor:
+    """pa_decode with a sliding window (0 = none), optional per-head ALiBi slopes (float32
+    GPU tensor [num_heads]) and the shared-blocks scheduling hint (same results, faster when
+    neighbouring sequences share blocks)."""
     nb, bs, h, d, dt = _check_pool(k_pool, v_pool)
     S = context_lens.shape[0]
     T = q.shape[0]
@@ -151,7 +153,8 @@ def pa_decode_ext(out, q, k_pool, v_pool, block_tables, context_lens, q_start_lo
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), nb, _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), _ptr(q_start_loc), S, T, int(max_context_len),
         int(max_query_len), h, d, bs, dt, _ptr(workspace), ws_bytes, int(sliding_window),
-        _ptr(alibi_slopes), _stream(stream))
+        _ptr(alibi_slopes), _lib.PA_DECODE_SHARED_BLOCKS if shared_blocks else 0,
+        _stream(stream))
     _lib.check(st, "pa_decode")
     return out
 

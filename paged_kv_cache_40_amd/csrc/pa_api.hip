@@ -135,7 +135,7 @@ int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
   return pa_decode_ext(out, q, k_pool, v_pool, num_blocks, block_tables, max_blocks_per_seq,
                        context_lens, q_start_loc, num_seqs, num_tokens, max_context_len,
                        max_query_len, num_heads, head_dim, block_size, dtype, workspace,
-                       workspace_bytes, 0, nullptr, stream);
+                       workspace_bytes, 0, nullptr, 0, stream);
 }
 
 int pa_decode_ext(void* out, const void* q, const void* k_pool, const void* v_pool,
@@ -144,9 +144,10 @@ int pa_decode_ext(void* out, const void* q, const void* k_pool, const void* v_po
                   int32_t num_tokens, int32_t max_context_len, int32_t max_query_len,
                   int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t dtype,
                   void* workspace, size_t workspace_bytes, int32_t sliding_window,
-                  const float* alibi_slopes, void* stream) {
+                  const float* alibi_slopes, uint32_t flags, void* stream) {
   if (int st = check_layout(num_blocks, num_heads, head_dim, block_size, dtype)) return st;
   if (sliding_window < 0) return PA_ERR_SHAPE;
+  if (flags & ~static_cast<uint32_t>(PA_DECODE_SHARED_BLOCKS)) return PA_ERR_UNSUPPORTED;
   // the multi-query tile path has no window / bias variant
   if (max_query_len > 1 && (sliding_window > 0 || alibi_slopes != nullptr))
     return PA_ERR_UNSUPPORTED;
@@ -160,6 +161,12 @@ int pa_decode_ext(void* out, const void* q, const void* k_pool, const void* v_po
     return PA_ERR_SHAPE;
   // grid limits of the decode launch: z = sequences, y = context partitions
   if (num_seqs > 65535 || max_context_len / pa::kMinPartition >= 65535) return PA_ERR_SHAPE;
+  // shared-block mode launches one-dimensionally: (head groups x sequences x partitions)
+  // workgroups of 256 work-items must stay below 2^32 work-items
+  if ((flags & PA_DECODE_SHARED_BLOCKS) &&
+      static_cast<int64_t>(num_heads) * num_seqs *
+              ((max_context_len + pa::kMinPartition - 1) / pa::kMinPartition) >= (int64_t{1} << 24))
+    return PA_ERR_SHAPE;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PA_ERR_NULL;
   // the multi-query tile path is built for fp16 with head_dim 128
   if (max_query_len > 1 && (dtype != PA_F16 || head_dim != 128)) return PA_ERR_UNSUPPORTED;
@@ -185,6 +192,7 @@ int pa_decode_ext(void* out, const void* q, const void* k_pool, const void* v_po
   a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(head_dim)));
   a.window = sliding_window;
   a.alibi = alibi_slopes;
+  a.flags = flags;
   a.workspace = workspace;
   hipStream_t st = static_cast<hipStream_t>(stream);
   // single-query sequences: context partitions + merge; the kernels skip the others

@@ -80,12 +80,15 @@ namespace pa {
 static_assert(PA_DECODE_PARTITION == 0 || PA_DECODE_PARTITION >= kMinPartition,
               "partition below the workspace sizing");
 
+// K/V loads.  Unshared batches stream (each row is read once: the non-temporal hint keeps it
+// from displacing useful lines); batches whose neighbouring sequences share blocks keep the
+// rows cached so the sharers find them in L2.
+template <bool kShared>
 __device__ __forceinline__ u32x4 ld_kv(const void* p) {
 #if PA_DECODE_NT_LOADS
-  return ld16_stream(p);
-#else
-  return ld16(p);
+  if constexpr (!kShared) return ld16_stream(p);
 #endif
+  return ld16(p);
 }
 
 template <typename T, int D, int BS, int P>
@@ -112,18 +115,44 @@ struct DecodeCfg {
 constexpr float kTau = 8.0f;  // log2 headroom before the running reference moves
 
 constexpr int kHeadsPerWg = PA_DECODE_HEADS_PER_WG;
+constexpr int kXcds = 8;  // accelerator complex dies of an MI355X
+#ifndef PA_DECODE_XCD_CHUNK
+#define PA_DECODE_XCD_CHUNK 128  // work units per run on one XCD (shared-block mode)
+#endif
+constexpr int kXcdChunk = PA_DECODE_XCD_CHUNK;
 
-template <typename T, int D, int BS, int P>
+template <typename T, int D, int BS, int P, bool kShared>
 __global__ __launch_bounds__(64 * kHeadsPerWg) PA_DECODE_OCCUPANCY
 void decode_partition_kernel(DecodeArgs a) {
   using C = DecodeCfg<T, D, BS, P>;
+  int hg, s, part;
+  if constexpr (kShared) {
+    // One-dimensional grid.  Workgroups go to the 8 XCDs round-robin by linear id; here runs
+    // of kXcdChunk consecutive work units (head group fastest, then sequence, then partition)
+    // stay on one XCD and the runs rotate over the XCDs, so neighbouring sequences - the
+    // samples or beams that share blocks - run on one XCD at about the same time and meet
+    // their shared rows in its L2, while every XCD still gets a share of the whole batch.
+    const int hgroups = (a.num_heads + kHeadsPerWg - 1) / kHeadsPerWg;
+    const int lin = blockIdx.x;
+    const int round = kXcds * kXcdChunk;
+    const int full = static_cast<int>(gridDim.x) / round * round;
+    int n = lin;
+    if (lin < full) {
+      const int xcd = lin % kXcds, k = lin / kXcds;
+      n = ((k / kXcdChunk) * kXcds + xcd) * kXcdChunk + k % kXcdChunk;
+    }
+    hg = n % hgroups;
+    s = (n / hgroups) % a.num_seqs;
+    part = n / (hgroups * a.num_seqs);
+  } else {
 #if PA_DECODE_GRID_ORDER == 1
-  const int part = blockIdx.x, hg = blockIdx.y, s = blockIdx.z;
+    part = blockIdx.x, hg = blockIdx.y, s = blockIdx.z;
 #elif PA_DECODE_GRID_ORDER == 2
-  const int hg = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
+    hg = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
 #else
-  const int hg = blockIdx.x, part = blockIdx.y, s = blockIdx.z;
+    hg = blockIdx.x, part = blockIdx.y, s = blockIdx.z;
 #endif
+  }
   const int h = hg * kHeadsPerWg + static_cast<int>(threadIdx.x >> 6);
   if (h >= a.num_heads) return;
   const int lane = threadIdx.x & 63;
@@ -252,12 +281,12 @@ void decode_partition_kernel(DecodeArgs a) {
     for (int i = 0; i < C::kG; ++i) {
       off[i] = row_offset(trip * C::kTrip + i * 8);
 #pragma unroll
-      for (int j = 0; j < C::kCpt; ++j) kr[i][j] = ld_kv(kbase + off[i] + col(j));
+      for (int j = 0; j < C::kCpt; ++j) kr[i][j] = ld_kv<kShared>(kbase + off[i] + col(j));
     }
 #pragma unroll
     for (int i = 0; i < C::kG; ++i)
 #pragma unroll
-      for (int j = 0; j < C::kCpt; ++j) vr[i][j] = ld_kv(vbase + off[i] + col(j));
+      for (int j = 0; j < C::kCpt; ++j) vr[i][j] = ld_kv<kShared>(vbase + off[i] + col(j));
     float sc[C::kG];
     bool ok[C::kG];
     // Only the trips that begin before the window's first token mask anything (the window's
@@ -297,9 +326,9 @@ void decode_partition_kernel(DecodeArgs a) {
         const int64_t off = row_offset(base);
         if (ok[i]) {
 #pragma unroll
-          for (int j = 0; j < C::kCpt; ++j) kr[i][j] = ld_kv(kbase + off + col(j));
+          for (int j = 0; j < C::kCpt; ++j) kr[i][j] = ld_kv<kShared>(kbase + off + col(j));
 #pragma unroll
-          for (int j = 0; j < C::kCpt; ++j) vr[i][j] = ld_kv(vbase + off + col(j));
+          for (int j = 0; j < C::kCpt; ++j) vr[i][j] = ld_kv<kShared>(vbase + off + col(j));
         }
       }
     }
@@ -417,15 +446,21 @@ static hipError_t launch_decode_t(const DecodeArgs& a0, int max_context_len, hip
   a.ws_acc = static_cast<float*>(a.workspace);
   a.ws_ml = a.ws_acc + static_cast<int64_t>(a.num_tokens) * a.num_heads * nparts * D;
   const int hgroups = (a.num_heads + kHeadsPerWg - 1) / kHeadsPerWg;
+  if (a.flags & kDecodeSharedBlocks) {
+    dim3 grid1(static_cast<unsigned>(hgroups) * a.num_seqs * nparts);
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, BS, P, true>), grid1,
+                       dim3(kWave * kHeadsPerWg), 0, stream, a);
+  } else {
 #if PA_DECODE_GRID_ORDER == 1
-  dim3 grid1(nparts, hgroups, a.num_seqs);
+    dim3 grid1(nparts, hgroups, a.num_seqs);
 #elif PA_DECODE_GRID_ORDER == 2
-  dim3 grid1(hgroups, a.num_seqs, nparts);
+    dim3 grid1(hgroups, a.num_seqs, nparts);
 #else
-  dim3 grid1(hgroups, nparts, a.num_seqs);
+    dim3 grid1(hgroups, nparts, a.num_seqs);
 #endif
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, BS, P>), grid1, dim3(kWave * kHeadsPerWg), 0,
-                     stream, a);
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, BS, P, false>), grid1,
+                       dim3(kWave * kHeadsPerWg), 0, stream, a);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nparts <= 1) return err;
   dim3 grid2(a.num_heads, a.num_seqs);

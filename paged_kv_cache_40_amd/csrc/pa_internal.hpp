@@ -7,6 +7,9 @@
 
 namespace pa {
 
+// DecodeArgs::flags: neighbouring sequences share blocks (cached loads, XCD-grouped launch)
+constexpr uint32_t kDecodeSharedBlocks = 1u;
+
 struct DecodeArgs {
   void* out;
   const void* q;
@@ -25,6 +28,7 @@ struct DecodeArgs {
   float scale_log2;        // log2(e) / sqrt(head_dim)
   int32_t window;          // sliding window in tokens (0 = none)
   const float* alibi;      // per-head ALiBi slopes [num_heads] or nullptr
+  uint32_t flags;          // kDecode* bits
   void* workspace;         // caller's scratch (see decode_workspace_bytes)
   // set by the launcher:
   int32_t num_parts_max;   // partition slots per (query row, head) in the workspace

@@ -22,17 +22,18 @@ def log(msg: str) -> None:
     print(msg, flush=True)
 
 
-def run_library(w, t, stream=None, workspace=None, window=0, alibi=None):
+def run_library(w, t, stream=None, workspace=None, window=0, alibi=None, shared=False):
     """copy-on-write copies -> slot writes -> attention, in stream order. Returns out.
 
-    window / alibi (host float slopes [H]) select the pa_decode_ext variants."""
+    window / alibi (host float slopes [H]) / shared (the shared-blocks hint) select
+    pa_decode_ext."""
     if w.copy_pairs is not None and len(w.copy_pairs):
         api.pa_copy_blocks(t["k_pool"], t["v_pool"], t["copy_pairs"], stream=stream)
     if w.num_writes:
         api.pa_write_kv(t["k_pool"], t["v_pool"], t["k_new"], t["v_new"], t["block_tables"],
                         t["context_lens"], t["write_start_loc"], stream=stream)
     out = torch.empty_like(t["q"])
-    if window == 0 and alibi is None:
+    if window == 0 and alibi is None and not shared:
         api.pa_decode(out, t["q"], t["k_pool"], t["v_pool"], t["block_tables"],
                       t["context_lens"], t["q_start_loc"], max_context_len=w.max_context_len,
                       max_query_len=w.max_query_len, workspace=workspace, stream=stream)
@@ -42,7 +43,8 @@ def run_library(w, t, stream=None, workspace=None, window=0, alibi=None):
         api.pa_decode_ext(out, t["q"], t["k_pool"], t["v_pool"], t["block_tables"],
                           t["context_lens"], t["q_start_loc"], max_context_len=w.max_context_len,
                           max_query_len=w.max_query_len, workspace=workspace,
-                          sliding_window=window, alibi_slopes=slopes, stream=stream)
+                          sliding_window=window, alibi_slopes=slopes, shared_blocks=shared,
+                          stream=stream)
     return out
 
 

@@ -78,13 +78,13 @@ def decode(lib, **kw):
                          a["dt"], a["ws"], a["wsb"], None)
 
 
-def decode_ext(lib, window=0, alibi=None, **kw):
+def decode_ext(lib, window=0, alibi=None, flags=0, **kw):
     a = dict(o=FAKE, q=FAKE, k=FAKE, v=FAKE, nb=64, bt=FAKE, mb=8, cl=FAKE, qsl=None, S=4, T=4,
              mcl=100, mql=1, H=2, D=64, B=16, dt=0, ws=FAKE, wsb=1 << 30)
     a.update(kw)
     return lib.pa_decode_ext(a["o"], a["q"], a["k"], a["v"], a["nb"], a["bt"], a["mb"], a["cl"],
                              a["qsl"], a["S"], a["T"], a["mcl"], a["mql"], a["H"], a["D"], a["B"],
-                             a["dt"], a["ws"], a["wsb"], window, alibi, None)
+                             a["dt"], a["ws"], a["wsb"], window, alibi, flags, None)
 
 
 @pytest.mark.parametrize("args,code", [
@@ -92,6 +92,8 @@ def decode_ext(lib, window=0, alibi=None, **kw):
     (dict(window=8, mql=2, qsl=FAKE, T=5, dt=1, D=128), -3),      # no multi-query variant
     (dict(alibi=FAKE, mql=2, qsl=FAKE, T=5, dt=1, D=128), -3),
     (dict(window=8, o=None), -1), (dict(alibi=FAKE, D=32), -3), (dict(window=8, mcl=129), -2),
+    (dict(flags=2), -3), (dict(flags=1 << 31), -3),
+    (dict(flags=1, H=64, S=65535, T=65535, mcl=2048, mb=128), -2),     # 1-D grid too large
 ])
 def test_decode_ext_rejects(lib, args, code):
     assert decode_ext(lib, **args) == code

@@ -119,6 +119,12 @@ class Workload:
             used.update(int(x) for x in self.block_tables[s, :nb])
         return len(used)
 
+    def shares_blocks(self) -> bool:
+        """Whether any physical block is read by more than one sequence."""
+        B = self.block_size
+        total = sum(-(-int(L) // B) for L in self.context_lens)
+        return self.unique_blocks_read() < total
+
     # ----- tensors -------------------------------------------------------
     def pool_shape(self):
         return (self.num_blocks, self.block_size, self.num_heads, self.head_dim)
