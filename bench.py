@@ -73,7 +73,7 @@ def hbm_stream_read_gbs(buf, reps: int = 5) -> float:
     lib.pa_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                          ctypes.c_int32, ctypes.c_void_p]
     nbytes = (buf.numel() * buf.element_size()) // 16 * 16
-    blocks = 256 * 32
+    blocks = 2048  # 8 workgroups per CU, each streaming whole 256 KB chunks
     out = torch.empty(blocks * 256, dtype=torch.int32, device=buf.device)
     stream = torch.cuda.current_stream()
     times = []

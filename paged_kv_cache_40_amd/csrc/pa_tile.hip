@@ -16,18 +16,29 @@
 // wave w owns queries q0+32w .. q0+32w+31 as two 16-query column tiles, so
 // every operand it reads from LDS feeds two matrix products.  Keys are
 // processed 32 per step:
-//   * the workgroup stages the step's K and V rows into LDS row-major
-//     ([key][dim], padded rows), double-buffered with one barrier per step,
-//     while the next step's rows are already in flight to registers;
-//   * S^T = K . Q^T per 16-key subtile and query tile: four
-//     v_mfma_f32_16x16x32_f16 over head_dim 128; lane (g, r) = (l/16, l%16)
-//     holds S^T[key 4g+i][query r], so every per-query quantity lives in the
-//     lanes of one column;
+//   * the workgroup stages each step's K and V rows into LDS row-major
+//     ([key][dim], padded rows) in a ring of three buffers: while a step's
+//     values are consumed, the next step's keys are already in LDS and the
+//     step after that is being written, so one barrier per step suffices; the
+//     global loads for a step are issued a whole step before they are staged.
+//     Each wave stages 8 consecutive rows of a step, which lie in one block
+//     (block sizes are multiples of 8), so its block id is a scalar load and
+//     every pool address is a scalar block base plus a fixed per-lane offset;
+//   * LDS pointers stay in the LDS address space and each step's base is
+//     formed once, so every LDS access of a step is that base plus an
+//     immediate offset (no per-access address arithmetic);
+//   * the loop is software-pipelined: the scores of step i+1,
+//     S^T = K . Q^T (four v_mfma_f32_16x16x32_f16 per 16-key subtile and query
+//     tile over head_dim 128), are issued in the same block as the
+//     exponentials of step i, so the matrix cores and the vector ALU work on
+//     independent data.  Lane (g, r) = (l/16, l%16) holds S^T[key 4g+i][query r];
 //   * causal masking by absolute key position, applied only on steps that
-//     reach a query's own position; online softmax with scores kept in raw
-//     units and the scale folded into one FMA, p = 2^(s*c - m*c) with
-//     c = log2(e)/sqrt(d), so masked scores (-inf) give p = 0 directly; the
-//     running reference m moves only when a score passes it by 2^8 in p;
+//     reach a wave's first query position; online softmax with scores kept in
+//     raw units and the scale folded into one FMA, p = 2^(s*c - m*c) with
+//     c = log2(e)/sqrt(d), so masked scores (-inf) give p = 0 directly.  The
+//     running reference m of a query moves only when one of its scores passes
+//     it by 2^8 in p: each lane checks its own scores and only a wave vote
+//     that finds such a score runs the cross-lane maximum and the rescale;
 //     P^T rounded to fp16;
 //   * O^T += V^T . P^T with v_mfma_f32_16x16x32_f16 over the step's 32 keys.
 //     The V^T operand comes straight from the row-major V rows through the
@@ -42,10 +53,9 @@
 //     constant operand whose row 0 is all ones, so it sums exactly the
 //     fp16-rounded P values the value product uses, on the matrix cores.
 // Accumulators live in VGPRs (the build passes -amdgpu-mfma-vgpr-form for
-// this file); the last query tiles, which see the most keys, are dispatched
-// first.
-// Values of keys at or past the context length are zeroed when staged (those
-// pool slots may hold anything), keys past a query's position are masked.
+// this file).  Values of keys at or past the context length are zeroed when
+// staged (those pool slots may hold anything); keys past a query's position
+// are masked.  Waves whose queries all lie past the chunk's end only stage.
 
 #include <math.h>
 
@@ -57,42 +67,45 @@ namespace pa {
 namespace {
 
 constexpr int kTileQ = 128;       // queries per workgroup (4 waves x 2 column tiles)
-#ifndef PA_TILE_STEP
-#define PA_TILE_STEP 32
-#endif
-constexpr int kStep = PA_TILE_STEP;  // keys per step (a multiple of 32)
-constexpr int kGroups = kStep / 32;  // 32-key groups per step
-static_assert(kStep % 32 == 0, "steps hold whole 32-key groups");
+constexpr int kStep = 32;         // keys per step
 constexpr int kD = 128;           // head dim of the tile path
 constexpr int kKRow = kD + 8;     // K row stride in LDS (halves): 272 B, 16-byte reads spread banks
 constexpr int kVRow = kD + 16;    // V row stride in LDS (halves): 288 B, transposing reads spread banks
 constexpr int kKBuf = kStep * kKRow;
 constexpr int kVBuf = kStep * kVRow;
-
-#ifndef PA_TILE_NT_LOADS
-#define PA_TILE_NT_LOADS 0  // K/V rows are re-read by every query tile of a head: keep them cached
-#endif
-#ifndef PA_TILE_BULK_LDS
-#define PA_TILE_BULK_LDS 0  // 1: read all LDS operands of a step before its products
-#endif
-#ifndef PA_TILE_HEAVY_FIRST
-#define PA_TILE_HEAVY_FIRST 1  // dispatch the last query tiles (most keys) first
-#endif
+constexpr int kBufs = 3;          // LDS ring: values of step i, keys of i+1, staging of i+2
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef __fp16 lds_f16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 
+// LDS pointers are kept in the LDS address space, so constant offsets fold into the
+// instructions' offset fields.
+typedef __attribute__((address_space(3))) f16 lf16;
+typedef __attribute__((address_space(3))) f16x8 lf16x8;
+typedef __attribute__((address_space(3))) u32x4 lu32x4;
+typedef __attribute__((address_space(3))) lds_f16x4 llds_f16x4;
+
 // Transposing 8-byte LDS read (see the lane mapping above).
-__device__ __forceinline__ f16x4 lds_read_tr(const f16* p) {
-  typedef __attribute__((address_space(3))) lds_f16x4* lptr;
-  const lds_f16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lptr)(p));
+__device__ __forceinline__ f16x4 lds_read_tr(const lf16* p) {
+  const lds_f16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4f16((llds_f16x4*)(p));
   return __builtin_bit_cast(f16x4, v);
+}
+
+// The per-step LDS base, computed once and hidden from reassociation, so every read of the
+// step is that base plus an immediate offset.
+__device__ __forceinline__ const lf16* opaque(const lf16* p) {
+  asm("" : "+v"(p));
+  return p;
+}
+
+__device__ __forceinline__ f32x4v mfma16(const f16x8& a, const f16x8& b, const f32x4v& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 }  // namespace
 
 #ifndef PA_TILE_WAVES_PER_EU
-#define PA_TILE_WAVES_PER_EU 2  // 3 per SIMD spills registers and runs slower
+#define PA_TILE_WAVES_PER_EU 2
 #endif
 #if PA_TILE_WAVES_PER_EU > 0
 #define PA_TILE_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_TILE_WAVES_PER_EU)))
@@ -102,18 +115,19 @@ __device__ __forceinline__ f16x4 lds_read_tr(const f16* p) {
 
 template <int BS>
 __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(TileArgs a) {
-  __shared__ __attribute__((aligned(16))) f16 lds_k[2][kKBuf];
-  __shared__ __attribute__((aligned(16))) f16 lds_v[2][kVBuf];
+  static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
+  constexpr int kTab = kStep / BS;  // blocks spanned by one step
+  __shared__ __attribute__((aligned(16))) f16 lds_k_[kBufs * kKBuf];
+  __shared__ __attribute__((aligned(16))) f16 lds_v_[kBufs * kVBuf];
+  lf16* const lds_k = (lf16*)(lds_k_);
+  lf16* const lds_v = (lf16*)(lds_v_);
 
+  // head fastest, then query tile (the last tiles, which see the most keys, first), then sequence
   const int h = blockIdx.x;
-#if PA_TILE_HEAVY_FIRST
   const int tile = static_cast<int>(gridDim.y) - 1 - static_cast<int>(blockIdx.y);
-#else
-  const int tile = blockIdx.y;
-#endif
   const int s = blockIdx.z;
   const int t = threadIdx.x;
-  const int w = t >> 6;
+  const int w = t >> 6;  // wave index
   const int l = t & 63;
   const int lg = l >> 4;  // lane group 0..3
   const int lr = l & 15;  // column within a 16-query tile
@@ -133,10 +147,12 @@ __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(T
     q[qt] = q0 + 32 * w + 16 * qt + lr;
     pos[qt] = q[qt] < n ? ctx - n + q[qt] : -1;
   }
-  // last key any query of the workgroup / of this wave needs
+  // last key any query of the workgroup / of this wave needs (-1: the wave has no query)
   const int wg_last = ctx - n + min(q0 + kTileQ - 1, n - 1);
-  const int wave_last = ctx - n + min(q0 + 32 * w + 31, n - 1);
+  const int wave_last = q0 + 32 * w < n ? ctx - n + min(q0 + 32 * w + 31, n - 1) : -1;
   const int nsteps = wg_last / kStep + 1;
+  // first query position of this wave: steps ending at or before it need no mask
+  const int wave_first_pos = ctx - n + q0 + 32 * w;
 
   // Q^T operands: lane (lg, lr) holds dims 8*lg + 32*st .. +7 of its query, st = 0..3
   f16x8 qop[2][4];
@@ -156,43 +172,53 @@ __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(T
   const f16* kpool = static_cast<const f16*>(a.k_pool) + static_cast<int64_t>(h) * kD;
   const f16* vpool = static_cast<const f16*>(a.v_pool) + static_cast<int64_t>(h) * kD;
   const int32_t* btrow = a.block_tables + static_cast<int64_t>(s) * a.max_blocks;
+  const int last_blk = (ctx - 1) / BS;
 
-  // staging: thread -> rows 16r + t/16 (r = 0..kStep/16-1) of the step, 16-byte chunk t%16
-  constexpr int kRows = kStep / 16;
-  const int st_row = t >> 4, st_chunk = t & 15;
-  u32x4 k_reg[kRows], v_reg[kRows];
-  // block ids of the rows this thread stages, looked up one step ahead of their use
-  int blk_next[kRows];
-  auto lookup = [&](int step) {
+  // Staging: wave ws stages rows 8*ws + 4*r + l/16 (r = 0, 1) of each step, 16-byte chunk l%16,
+  // so the four rows of one load instruction, and both of its instructions, lie in one block
+  // (block sizes are multiples of 8): the block id is wave-uniform and the pool address is a
+  // scalar block base plus a fixed per-lane offset.
+  const int ws = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int srow = 8 * ws + (l >> 4);  // this lane's first staged row
+  const int schunk = l & 15;
+  const int64_t block_elems = static_cast<int64_t>(BS) * row_stride;
+  const uint32_t toff0 = static_cast<uint32_t>(((srow % BS) * row_stride + 8 * schunk) * 2);
+  const uint32_t toff1 = static_cast<uint32_t>((((srow + 4) % BS) * row_stride + 8 * schunk) * 2);
+  const char* kpool_b = reinterpret_cast<const char*>(kpool);
+  const char* vpool_b = reinterpret_cast<const char*>(vpool);
+  u32x4 k_reg[2], v_reg[2];
+  // block id of this wave's rows in `step` (clamped to the last used block; invalid ids
+  // read block 0, so every address stays inside the pool)
+  const uint32_t nblk32 =
+      static_cast<uint32_t>(a.num_blocks < INT32_MAX ? a.num_blocks : INT32_MAX);
+  auto block_of = [&](int step) {
+    const int idx = min(step * kTab + (8 * ws) / BS, last_blk);
+    const int b = btrow[idx];
+    return static_cast<uint32_t>(b) < nblk32 ? b : 0;
+  };
+  auto fetch = [&](int step, int blk) {
+    const int64_t boff = static_cast<int64_t>(blk) * block_elems * 2;
+    const char* kb = kpool_b + boff;
+    const char* vb = vpool_b + boff;
+    k_reg[0] = ld16(kb + toff0);
+    v_reg[0] = ld16(vb + toff0);
+    k_reg[1] = ld16(kb + toff1);
+    v_reg[1] = ld16(vb + toff1);
+    if (step * kStep + kStep > ctx) {  // the step holding the context's end (wave-uniform)
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-      const int key = min(step * kStep + 16 * r + st_row, ctx - 1);
-      const int b = btrow[key / BS];
-      blk_next[r] = (b >= 0 && b < a.num_blocks) ? b : 0;
+      for (int r = 0; r < 2; ++r)
+        if (step * kStep + srow + 4 * r >= ctx) v_reg[r] = u32x4{0, 0, 0, 0};
     }
   };
-  auto fetch = [&](int step) {
-#pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-      const int key = step * kStep + 16 * r + st_row;
-      const int64_t row =
-          (static_cast<int64_t>(blk_next[r]) * BS + min(key, ctx - 1) % BS) * row_stride;
-#if PA_TILE_NT_LOADS
-      k_reg[r] = ld16_stream(kpool + row + 8 * st_chunk);
-      const u32x4 v = ld16_stream(vpool + row + 8 * st_chunk);
-#else
-      k_reg[r] = ld16(kpool + row + 8 * st_chunk);
-      const u32x4 v = ld16(vpool + row + 8 * st_chunk);
-#endif
-      v_reg[r] = key < ctx ? v : u32x4{0, 0, 0, 0};  // keys past the context: zero values
-    }
-  };
+  const int kst_off = srow * kKRow + 8 * schunk;
+  const int vst_off = srow * kVRow + 8 * schunk;
   auto stage = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-      *reinterpret_cast<u32x4*>(&lds_k[buf][(16 * r + st_row) * kKRow + 8 * st_chunk]) = k_reg[r];
-      *reinterpret_cast<u32x4*>(&lds_v[buf][(16 * r + st_row) * kVRow + 8 * st_chunk]) = v_reg[r];
-    }
+    lf16* kd = lds_k + buf * kKBuf + kst_off;
+    lf16* vd = lds_v + buf * kVBuf + vst_off;
+    *(lu32x4*)(kd) = k_reg[0];
+    *(lu32x4*)(vd) = v_reg[0];
+    *(lu32x4*)(kd + 4 * kKRow) = k_reg[1];
+    *(lu32x4*)(vd + 4 * kVRow) = v_reg[1];
   };
 
   // Scores stay in raw units (q.k); c = log2(e)/sqrt(d) is folded into one FMA with the
@@ -213,83 +239,53 @@ __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(T
   f16x8 ones_op;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones_op[e] = static_cast<f16>(lr == 0 ? 1.f : 0.f);
-  // first query position of this wave: steps ending at or before it need no mask
-  const int wave_first_pos = ctx - n + q0 + 32 * w;
 
-  lookup(0);
-  fetch(0);
-  if (nsteps > 1) lookup(1);
-  for (int step = 0; step < nsteps; ++step) {
-    const int buf = step & 1;
-    stage(buf);
-    __syncthreads();
-    if (step + 1 < nsteps) {
-      fetch(step + 1);
-      if (step + 2 < nsteps) lookup(step + 2);
-    }
-    const int base = step * kStep;
-    if (base > wave_last) continue;  // every query of this wave precedes the step
+  const lf16* const kbase = lds_k + lr * kKRow + 8 * lg;
+  const lf16* const vbase = lds_v + (4 * lg + (lr >> 2)) * kVRow + 4 * (lr & 3);
 
-    // S^T for the step's 16-key subtiles x two query tiles
-    constexpr int kSub = 2 * kGroups;
-    f32x4v sc[2][kSub];
+  // S^T of one step for both query tiles: sc[qt][sub] holds keys 16*sub + 4*lg + i
+  auto scores = [&](int buf, f32x4v (&sc)[2][2]) {
+    const lf16* kb = opaque(kbase + buf * kKBuf);
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-      for (int sub = 0; sub < kSub; ++sub) sc[qt][sub] = f32x4v{0.f, 0.f, 0.f, 0.f};
-#if PA_TILE_BULK_LDS
-    f16x8 kops[kSub][4];
+      for (int sub = 0; sub < 2; ++sub) sc[qt][sub] = f32x4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int sub = 0; sub < kSub; ++sub)
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-        kops[sub][st] = *reinterpret_cast<const f16x8*>(
-            &lds_k[buf][(16 * sub + lr) * kKRow + 8 * lg + 32 * st]);
-#pragma unroll
-    for (int st = 0; st < 4; ++st)
-#pragma unroll
-      for (int sub = 0; sub < kSub; ++sub)
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-          sc[qt][sub] =
-              __builtin_amdgcn_mfma_f32_16x16x32_f16(kops[sub][st], qop[qt][st], sc[qt][sub], 0, 0, 0);
-#else
-#pragma unroll
-    for (int sub = 0; sub < kSub; ++sub)
+    for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const f16x8 kop = *reinterpret_cast<const f16x8*>(
-            &lds_k[buf][(16 * sub + lr) * kKRow + 8 * lg + 32 * st]);
+        const f16x8 kop = *(const lf16x8*)(kb + (16 * sub) * kKRow + 32 * st);
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-          sc[qt][sub] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[qt][st], sc[qt][sub], 0, 0, 0);
+        for (int qt = 0; qt < 2; ++qt) sc[qt][sub] = mfma16(kop, qop[qt][st], sc[qt][sub]);
       }
-#endif
-    // mask keys past each query's position (only on steps that reach the diagonal)
-    if (base + kStep - 1 > wave_first_pos) {
+  };
+
+  // Causal mask and the reference update for the scores of the step at key `base`.
+  auto prepare = [&](int base, f32x4v (&sc)[2][2]) {
+    if (base + kStep - 1 > wave_first_pos) {  // the step reaches this wave's diagonal
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-        for (int sub = 0; sub < kSub; ++sub)
+        for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             if (base + 16 * sub + 4 * lg + i > pos[qt]) sc[qt][sub][i] = -INFINITY;
     }
-    float mx[2];
+    float lmax[2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-      mx[qt] = -INFINITY;
-#pragma unroll
-      for (int sub = 0; sub < kSub; ++sub)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx[qt] = fmaxf(mx[qt], sc[qt][sub][i]);
-      mx[qt] = fmaxf(mx[qt], shfl_xor_f(mx[qt], 16));
-      mx[qt] = fmaxf(mx[qt], shfl_xor_f(mx[qt], 32));
+      float v = fmaxf(fmaxf(sc[qt][0][0], sc[qt][0][1]), sc[qt][0][2]);
+      v = fmaxf(fmaxf(v, sc[qt][0][3]), sc[qt][1][0]);
+      v = fmaxf(fmaxf(v, sc[qt][1][1]), sc[qt][1][2]);
+      lmax[qt] = fmaxf(v, sc[qt][1][3]);
     }
-    if (__any(mx[0] > m[0] + tau || mx[1] > m[1] + tau)) {
+    if (__any(lmax[0] > m[0] + tau || lmax[1] > m[1] + tau)) {
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
-        const float mn = fmaxf(m[qt], mx[qt]);
+        float mx = lmax[qt];
+        mx = fmaxf(mx, shfl_xor_f(mx, 16));
+        mx = fmaxf(mx, shfl_xor_f(mx, 32));
+        const float mn = fmaxf(m[qt], mx);
         const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2((m[qt] - mn) * c);
         den[qt] *= alpha;
 #pragma unroll
@@ -298,49 +294,79 @@ __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(T
         mc[qt] = (mn == -INFINITY) ? 0.f : mn * c;
       }
     }
-    // P^T operands per (query tile, 32-key group G): keys 32G+4g+i then 32G+16+4g+i
-    f16x8 pop[2][kGroups];
+  };
+
+  // P^T operands (keys 4g+i then 16+4g+i) and O^T += V^T . P^T for the step in `buf`.
+  auto exps = [&](const f32x4v (&sc)[2][2], f16x8 (&pop)[2]) {
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-      for (int sub = 0; sub < kSub; ++sub)
+      for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          pop[qt][sub >> 1][4 * (sub & 1) + i] =
-              static_cast<f16>(fast_exp2(fmaf(sc[qt][sub][i], c, -mc[qt])));
-    // O^T += V^T . P^T, 16 head dims x 32 keys per product; the ones row sums P
+          pop[qt][4 * sub + i] = static_cast<f16>(fast_exp2(fmaf(sc[qt][sub][i], c, -mc[qt])));
+  };
+  auto values = [&](int buf, const f16x8 (&pop)[2]) {
+    const lf16* vrow0 = opaque(vbase + buf * kVBuf);
+    const lf16* vrow1 = vrow0 + 16 * kVRow;
 #pragma unroll
-    for (int G = 0; G < kGroups; ++G) {
-      const f16* vrow0 = &lds_v[buf][(32 * G + 4 * lg + (lr >> 2)) * kVRow + 4 * (lr & 3)];
-      const f16* vrow1 = vrow0 + 16 * kVRow;
+    for (int qt = 0; qt < 2; ++qt) den[qt] = mfma16(ones_op, pop[qt], den[qt]);
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-        den[qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones_op, pop[qt][G], den[qt], 0, 0, 0);
-#if PA_TILE_BULK_LDS
-      f16x8 vops[8];
+    for (int j = 0; j < 8; ++j) {
+      const f16x4 va = lds_read_tr(vrow0 + 16 * j);
+      const f16x4 vb = lds_read_tr(vrow1 + 16 * j);
+      const f16x8 vop = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const f16x4 va = lds_read_tr(vrow0 + 16 * j);
-        const f16x4 vb = lds_read_tr(vrow1 + 16 * j);
-        vops[j] = f16x8{va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-          acc[qt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vops[j], pop[qt][G], acc[qt][j], 0, 0, 0);
-#else
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const f16x4 va = lds_read_tr(vrow0 + 16 * j);
-        const f16x4 vb = lds_read_tr(vrow1 + 16 * j);
-        const f16x8 vop = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-          acc[qt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[qt][G], acc[qt][j], 0, 0, 0);
-      }
-#endif
+      for (int qt = 0; qt < 2; ++qt) acc[qt][j] = mfma16(vop, pop[qt], acc[qt][j]);
     }
+  };
+
+  int blk_next;  // block id of this wave's rows in the next step to fetch
+  // One pipelined step: values of `step` (scores in `cur`), scores of step+1 into `nxt`.
+  auto iteration = [&](int step, f32x4v (&cur)[2][2], f32x4v (&nxt)[2][2]) {
+    const int b_cur = step % kBufs;
+    const int b_nxt = (step + 1) % kBufs;
+    if (step + 2 < nsteps) stage((step + 2) % kBufs);
+    if (step + 3 < nsteps) {
+      fetch(step + 3, blk_next);
+      if (step + 4 < nsteps) blk_next = block_of(step + 4);
+    }
+    const int base = step * kStep;
+    if (base + kStep <= wave_last) {
+      prepare(base, cur);
+      f16x8 pop[2];
+      scores(b_nxt, nxt);
+      exps(cur, pop);
+      values(b_cur, pop);
+    } else if (base <= wave_last) {
+      prepare(base, cur);
+      f16x8 pop[2];
+      exps(cur, pop);
+      values(b_cur, pop);
+    }
+    __syncthreads();
+  };
+
+  // prologue: steps 0 and 1 staged, step 2 in flight, scores of step 0
+  blk_next = block_of(0);
+  fetch(0, blk_next);
+  stage(0);
+  if (nsteps > 1) {
+    fetch(1, block_of(1));
+    stage(1);
+  }
+  if (nsteps > 2) fetch(2, block_of(2));
+  if (nsteps > 3) blk_next = block_of(3);
+  __syncthreads();
+  f32x4v sa[2][2], sb[2][2];
+  if (wave_last >= 0) scores(0, sa);
+
+  for (int step = 0; step < nsteps; ++step) {
+    iteration(step, sa, sb);
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) sa[qt][sub] = sb[qt][sub];
   }
 
 #pragma unroll

@@ -304,6 +304,16 @@ def test_chunk_tiles_edges(B):
     full_check(w)
 
 
+@pytest.mark.parametrize("B", [8, 16, 32])
+def test_chunk_tiles_multi_tile(B):
+    """Chunks spanning three to four 128-query tiles, with priors that end mid-block and
+    mid-step, so the staged steps cross blocks at every offset and the last step of a tile
+    holds the context's end."""
+    chunks = [(37, 300), (1000, 257), (5, 511), (96, 384)]
+    w = make_custom_mixed(50 + B, 2, B, chunks, [7, 129], name=f"chunks_multi_B{B}")
+    full_check(w)
+
+
 def test_chunk_tiles_peaked_scores():
     w = make_custom_mixed(41, 3, 16, [(200, 100), (0, 70)], [50], name="chunks_peaked",
                           q_scale=4.0)
