@@ -69,7 +69,8 @@ namespace {
 constexpr int kTileQ = 128;       // queries per workgroup (4 waves x 2 column tiles)
 constexpr int kStep = 32;         // keys per step
 constexpr int kD = 128;           // head dim of the tile path
-constexpr int kKRow = kD + 8;     // K row stride in LDS (halves): 272 B, 16-byte reads spread banks
+constexpr int kKRow = kD + 16;    // K row stride in LDS (halves): 288 B; the 16-byte operand reads
+                                  // run at the full LDS rate with it (272 B measured half rate)
 constexpr int kVRow = kD + 16;    // V row stride in LDS (halves): 288 B, transposing reads spread banks
 constexpr int kKBuf = kStep * kKRow;
 constexpr int kVBuf = kStep * kVRow;
