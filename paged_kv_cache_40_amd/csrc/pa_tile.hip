@@ -362,13 +362,12 @@ __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(T
   f32x4v sa[2][2], sb[2][2];
   if (wave_last >= 0) scores(0, sa);
 
-  for (int step = 0; step < nsteps; ++step) {
+  int step = 0;
+  for (; step + 1 < nsteps; step += 2) {
     iteration(step, sa, sb);
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) sa[qt][sub] = sb[qt][sub];
+    iteration(step + 1, sb, sa);
   }
+  if (step < nsteps) iteration(step, sa, sb);
 
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
