@@ -628,7 +628,7 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
+        print(f"bench.py: the paged-attention path is measured on exactly one GPU; --gpus {args.gpus} is not "
               "supported (the path has no cross-GPU step to measure)", file=sys.stderr)
         return 2
 
