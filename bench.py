@@ -194,6 +194,10 @@ def bench_config(args) -> int:
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(t["q"])
     shared = w.shares_blocks() and not args.no_shared_hint
+    slopes = None
+    if args.alibi:  # the ALiBi paper's geometric slopes
+        slopes = torch.tensor(2.0 ** (-8.0 * (np.arange(w.num_heads) + 1) / w.num_heads),
+                              dtype=torch.float32, device="cuda")
 
     def step():
         if w.copy_pairs is not None and len(w.copy_pairs):
@@ -203,10 +207,16 @@ def bench_config(args) -> int:
                             t["context_lens"], t["write_start_loc"])
         api.pa_decode_ext(out, t["q"], t["k_pool"], t["v_pool"], t["block_tables"],
                           t["context_lens"], t["q_start_loc"], max_context_len=w.max_context_len,
-                          max_query_len=w.max_query_len, workspace=ws, shared_blocks=shared)
+                          max_query_len=w.max_query_len, workspace=ws, shared_blocks=shared,
+                          sliding_window=args.window, alibi_slopes=slopes)
 
     wall_ms, ev_ms = _timed(step, args.steps, args.warmup)
     kv = w.kv_bytes_read()
+    if args.window:  # K and V rows inside each query row's window, counted once per sequence
+        L = w.context_lens.astype(np.int64)
+        n = w.query_lens.astype(np.int64)
+        first = np.maximum(0, L - n - args.window + 1)
+        kv = int(2 * (L - first).sum() * w.num_heads * w.head_dim * w.elt_bytes)
     B = w.block_size
     unique = w.unique_blocks_read() * 2 * B * w.num_heads * w.head_dim * w.elt_bytes
     rec = {
@@ -219,7 +229,8 @@ def bench_config(args) -> int:
                    "num_blocks": w.num_blocks, "num_queries": w.num_queries,
                    "num_writes": w.num_writes,
                    "copy_pairs": 0 if w.copy_pairs is None else len(w.copy_pairs),
-                   "shared_blocks_hint": shared,
+                   "shared_blocks_hint": shared, "sliding_window": args.window,
+                   "alibi": bool(args.alibi),
                    "kv_bytes_logical": kv, "kv_bytes_unique_blocks": unique},
         "event_ms_per_step": round(ev_ms, 4),
         "pct_hbm_peak_logical": round(100 * kv / (wall_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
@@ -612,9 +623,11 @@ def main(argv=None) -> int:
     ap.add_argument("--sweep", action="store_true",
                     help="also print decode latency vs batch size, scattered vs identity tables")
     ap.add_argument("--window", type=int, default=0,
-                    help="time the large batch with this sliding window instead (own line)")
+                    help="sliding window: the large batch's own variant line, or applied to "
+                         "the batch of --config N")
     ap.add_argument("--alibi", action="store_true",
-                    help="time the large batch with ALiBi slopes instead (own line)")
+                    help="ALiBi slopes: the large batch's own variant line, or applied to the "
+                         "batch of --config N")
     ap.add_argument("--swap", action="store_true",
                     help="time pa_swap_blocks out and in against plain host-link copies (own line)")
     ap.add_argument("--swap-seqs", type=int, default=64)

@@ -119,7 +119,7 @@ size_t pa_decode_workspace_bytes(int32_t num_tokens, int32_t num_heads, int32_t 
  *   (chunked prefill mixed with decodes in one batch, P3 section
  *   "Chunked prefill"), each query attending to positions <= its own.
  * max_context_len, max_query_len: host copies of the maxima over the batch
- *   (grid sizing); max_query_len > 1 requires dtype PA_F16.
+ *   (grid sizing); max_query_len > 1 requires dtype PA_F16 and head_dim 128.
  * workspace: device scratch of at least
  *   pa_decode_workspace_bytes(num_tokens, num_heads, head_dim, max_context_len)
  *   bytes (NULL allowed when that is 0); contents on return are unspecified.
@@ -139,8 +139,13 @@ int pa_decode(void* out, const void* q,
  * ALiBi; P3 "메모리 관리": sliding layers keep a fixed window of the most
  * recent tokens).  The pages give no formulas; the readings implemented:
  *   sliding_window W > 0: the query at position p attends to tokens
- *     p-W+1 .. p only (W = 0: no window).  Blocks that hold only older tokens
- *     are never read.
+ *     p-W+1 .. p only (W = 0: no window).  Older tokens never contribute, and
+ *     the table entries of blocks that hold only tokens older than every
+ *     query's window may be -1: the single-query path never looks them up;
+ *     the multi-query path may look up the entries of the (at most three)
+ *     such blocks inside the 32-token step where a chunk's window starts,
+ *     fetches the named block (block 0 for an invalid entry) and discards
+ *     those rows.
  *   alibi_slopes: device float [num_heads] or NULL; slope_h * (j - p) is added
  *     to the score q.k_j / sqrt(head_dim) of token j (0 for the query itself,
  *     more negative with distance).
@@ -154,11 +159,11 @@ int pa_decode(void* out, const void* q,
  *   speed differs.  Unknown bits return PA_ERR_UNSUPPORTED; with the flag,
  *   num_heads * num_seqs * ceil(max_context_len / 256) must stay below 2^24
  *   (PA_ERR_SHAPE).
- * pa_decode(...) is pa_decode_ext(..., 0, NULL, 0, stream).  The window and
- * ALiBi variants are built for single-query sequences only: with
- * max_query_len > 1, a nonzero window or non-NULL slopes return
- * PA_ERR_UNSUPPORTED.  sliding_window < 0 returns PA_ERR_SHAPE.  The
- * workspace requirement is unchanged.
+ * pa_decode(...) is pa_decode_ext(..., 0, NULL, 0, stream).  Both variants
+ * apply to every query row, single-query decodes and multi-query chunks alike
+ * (a chunk's query at position p sees its own window p-W+1 .. p).
+ * sliding_window < 0 returns PA_ERR_SHAPE.  The workspace requirement is
+ * unchanged.
  */
 int pa_decode_ext(void* out, const void* q,
                   const void* k_pool, const void* v_pool, int64_t num_blocks,

@@ -148,9 +148,6 @@ int pa_decode_ext(void* out, const void* q, const void* k_pool, const void* v_po
   if (int st = check_layout(num_blocks, num_heads, head_dim, block_size, dtype)) return st;
   if (sliding_window < 0) return PA_ERR_SHAPE;
   if (flags & ~static_cast<uint32_t>(PA_DECODE_SHARED_BLOCKS)) return PA_ERR_UNSUPPORTED;
-  // the multi-query tile path has no window / bias variant
-  if (max_query_len > 1 && (sliding_window > 0 || alibi_slopes != nullptr))
-    return PA_ERR_UNSUPPORTED;
   if (num_seqs <= 0 || num_tokens <= 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
   if (max_context_len <= 0 || max_query_len <= 0 || max_query_len > max_context_len)
     return PA_ERR_SHAPE;
@@ -213,6 +210,8 @@ int pa_decode_ext(void* out, const void* q, const void* k_pool, const void* v_po
   ta.num_tokens = num_tokens;
   ta.num_heads = num_heads;
   ta.scale_log2 = a.scale_log2;
+  ta.window = sliding_window;
+  ta.alibi = alibi_slopes;
   return launch_status(pa::launch_tile(ta, head_dim, block_size, max_query_len, st));
 }
 

@@ -51,6 +51,8 @@ struct TileArgs {
   int32_t num_tokens;
   int32_t num_heads;
   float scale_log2;
+  int32_t window;          // sliding window in tokens (0 = none)
+  const float* alibi;      // per-head ALiBi slopes [num_heads] or nullptr
 };
 
 // Smallest context partition any decode launch uses; sizes the workspace.

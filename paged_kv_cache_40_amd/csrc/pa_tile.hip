@@ -69,6 +69,7 @@ namespace {
 constexpr int kTileQ = 128;       // queries per workgroup (4 waves x 2 column tiles)
 constexpr int kStep = 32;         // keys per step
 constexpr int kD = 128;           // head dim of the tile path
+constexpr float kSqrtD = 11.313708498984761f;  // sqrt(kD)
 constexpr int kKRow = kD + 16;    // K row stride in LDS (halves): 288 B; the 16-byte operand reads
                                   // run at the full LDS rate with it (272 B measured half rate)
 constexpr int kVRow = kD + 16;    // V row stride in LDS (halves): 288 B, transposing reads spread banks
@@ -114,7 +115,7 @@ __device__ __forceinline__ f32x4v mfma16(const f16x8& a, const f16x8& b, const f
 #define PA_TILE_OCCUPANCY
 #endif
 
-template <int BS>
+template <int BS, bool kWindow, bool kAlibi>
 __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(TileArgs a) {
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
   constexpr int kTab = kStep / BS;  // blocks spanned by one step
@@ -154,6 +155,18 @@ __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(T
   const int nsteps = wg_last / kStep + 1;
   // first query position of this wave: steps ending at or before it need no mask
   const int wave_first_pos = ctx - n + q0 + 32 * w;
+  // Sliding window W > 0: the query at position p sees keys p-W+1 .. p.  The workgroup starts
+  // at the step holding its first query's window start (older keys are never fetched for
+  // use); a wave computes only the steps from its own first query's window start to its last
+  // query.  Without a window every wave starts at step 0.
+  const int W = kWindow ? a.window : 0;  // compile-time 0 without a window
+  const int wg_key_lo = W > 0 ? max(0, ctx - n + q0 - W + 1) : 0;
+  const int step_lo = wg_key_lo / kStep;
+  const int wave_hi_step = wave_last >= 0 ? wave_last / kStep : -1;
+  const int wave_lo_step = W > 0 ? max(0, wave_first_pos - W + 1) / kStep : 0;
+  // ALiBi: slope_h * (j - p) is added to q.k_j / sqrt(d); in the raw units of the scores here
+  // (q.k) that is slope_h * sqrt(d) * (j - p).
+  const float slope_sd = kAlibi ? a.alibi[h] * kSqrtD : 0.f;
 
   // Q^T operands: lane (lg, lr) holds dims 8*lg + 32*st .. +7 of its query, st = 0..3
   f16x8 qop[2][4];
@@ -210,6 +223,11 @@ __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(T
       for (int r = 0; r < 2; ++r)
         if (step * kStep + srow + 4 * r >= ctx) v_reg[r] = u32x4{0, 0, 0, 0};
     }
+    if (step * kStep < wg_key_lo) {  // the step holding the window's start: older slots may
+#pragma unroll                       // hold anything (their blocks may even be released)
+      for (int r = 0; r < 2; ++r)
+        if (step * kStep + srow + 4 * r < wg_key_lo) v_reg[r] = u32x4{0, 0, 0, 0};
+    }
   };
   const int kst_off = srow * kKRow + 8 * schunk;
   const int vst_off = srow * kVRow + 8 * schunk;
@@ -244,13 +262,27 @@ __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(T
   const lf16* const kbase = lds_k + lr * kKRow + 8 * lg;
   const lf16* const vbase = lds_v + (4 * lg + (lr >> 2)) * kVRow + 4 * (lr & 3);
 
-  // S^T of one step for both query tiles: sc[qt][sub] holds keys 16*sub + 4*lg + i
-  auto scores = [&](int buf, f32x4v (&sc)[2][2]) {
+  // S^T of the step at key `base` for both query tiles: sc[qt][sub] holds keys
+  // base + 16*sub + 4*lg + i.  With ALiBi the accumulators start at the bias, so the products
+  // add q.k onto it.
+  auto scores = [&](int buf, int base, f32x4v (&sc)[2][2]) {
     const lf16* kb = opaque(kbase + buf * kKBuf);
+    if constexpr (kAlibi) {
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+      for (int qt = 0; qt < 2; ++qt) {
+        const float fd = static_cast<float>(base + 4 * lg - pos[qt]);  // j - p for sub = i = 0
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) sc[qt][sub] = f32x4v{0.f, 0.f, 0.f, 0.f};
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sc[qt][sub][i] = slope_sd * (fd + static_cast<float>(16 * sub + i));
+      }
+    } else {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) sc[qt][sub] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -261,16 +293,22 @@ __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(T
       }
   };
 
-  // Causal mask and the reference update for the scores of the step at key `base`.
+  // Causal (and window) mask and the reference update for the scores of the step at `base`.
   auto prepare = [&](int base, f32x4v (&sc)[2][2]) {
-    if (base + kStep - 1 > wave_first_pos) {  // the step reaches this wave's diagonal
+    // masking runs only on steps that reach this wave's diagonal or hold some query's window
+    // start
+    if (base + kStep - 1 > wave_first_pos || (W > 0 && base < wave_last - W + 1)) {
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+      for (int qt = 0; qt < 2; ++qt) {
+        const int lo = W > 0 ? pos[qt] - W + 1 : INT32_MIN;
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (base + 16 * sub + 4 * lg + i > pos[qt]) sc[qt][sub][i] = -INFINITY;
+          for (int i = 0; i < 4; ++i) {
+            const int key = base + 16 * sub + 4 * lg + i;
+            if (key > pos[qt] || key < lo) sc[qt][sub][i] = -INFINITY;
+          }
+      }
     }
     float lmax[2];
 #pragma unroll
@@ -324,45 +362,51 @@ __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(T
 
   int blk_next;  // block id of this wave's rows in the next step to fetch
   // One pipelined step: values of `step` (scores in `cur`), scores of step+1 into `nxt`.
+  // LDS buffers are numbered from the first step of the workgroup.
   auto iteration = [&](int step, f32x4v (&cur)[2][2], f32x4v (&nxt)[2][2]) {
-    const int b_cur = step % kBufs;
-    const int b_nxt = (step + 1) % kBufs;
-    if (step + 2 < nsteps) stage((step + 2) % kBufs);
+    const int rel = step - step_lo;
+    const int b_cur = rel % kBufs;
+    const int b_nxt = (rel + 1) % kBufs;
+    if (step + 2 < nsteps) stage((rel + 2) % kBufs);
     if (step + 3 < nsteps) {
       fetch(step + 3, blk_next);
       if (step + 4 < nsteps) blk_next = block_of(step + 4);
     }
     const int base = step * kStep;
-    if (base + kStep <= wave_last) {
+    const bool cur_on = step >= wave_lo_step && step <= wave_hi_step;
+    const bool nxt_on = step + 1 >= wave_lo_step && step + 1 <= wave_hi_step;
+    if (cur_on && nxt_on) {
       prepare(base, cur);
       f16x8 pop[2];
-      scores(b_nxt, nxt);
+      scores(b_nxt, base + kStep, nxt);
       exps(cur, pop);
       values(b_cur, pop);
-    } else if (base <= wave_last) {
+    } else if (cur_on) {
       prepare(base, cur);
       f16x8 pop[2];
       exps(cur, pop);
       values(b_cur, pop);
+    } else if (nxt_on) {  // the step before this wave's window: its first scores
+      scores(b_nxt, base + kStep, nxt);
     }
     __syncthreads();
   };
 
-  // prologue: steps 0 and 1 staged, step 2 in flight, scores of step 0
-  blk_next = block_of(0);
-  fetch(0, blk_next);
+  // prologue: the first two steps staged, the third in flight, scores of the first step
+  blk_next = block_of(step_lo);
+  fetch(step_lo, blk_next);
   stage(0);
-  if (nsteps > 1) {
-    fetch(1, block_of(1));
+  if (step_lo + 1 < nsteps) {
+    fetch(step_lo + 1, block_of(step_lo + 1));
     stage(1);
   }
-  if (nsteps > 2) fetch(2, block_of(2));
-  if (nsteps > 3) blk_next = block_of(3);
+  if (step_lo + 2 < nsteps) fetch(step_lo + 2, block_of(step_lo + 2));
+  if (step_lo + 3 < nsteps) blk_next = block_of(step_lo + 3);
   __syncthreads();
   f32x4v sa[2][2], sb[2][2];
-  if (wave_last >= 0) scores(0, sa);
+  if (wave_lo_step == step_lo && wave_hi_step >= step_lo) scores(0, step_lo * kStep, sa);
 
-  int step = 0;
+  int step = step_lo;
   for (; step + 1 < nsteps; step += 2) {
     iteration(step, sa, sb);
     iteration(step + 1, sb, sa);
@@ -392,12 +436,22 @@ hipError_t launch_tile(const TileArgs& a, int head_dim, int block_size, int max_
   if (head_dim != kD) return hipErrorInvalidValue;
   const int tiles = (max_query_len + kTileQ - 1) / kTileQ;
   dim3 grid(a.num_heads, tiles, a.num_seqs);
+  const bool window = a.window > 0;
+  const bool alibi = a.alibi != nullptr;
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a); };
+  // (window, ALiBi) pick one of four instantiations per block size
+#define PA_TILE_VARIANTS(B_)                                                  \
+  if (window && alibi) go(tile_attention_kernel<B_, true, true>);             \
+  else if (window) go(tile_attention_kernel<B_, true, false>);                \
+  else if (alibi) go(tile_attention_kernel<B_, false, true>);                 \
+  else go(tile_attention_kernel<B_, false, false>);
   switch (block_size) {
-    case 8: hipLaunchKernelGGL(tile_attention_kernel<8>, grid, dim3(256), 0, stream, a); break;
-    case 16: hipLaunchKernelGGL(tile_attention_kernel<16>, grid, dim3(256), 0, stream, a); break;
-    case 32: hipLaunchKernelGGL(tile_attention_kernel<32>, grid, dim3(256), 0, stream, a); break;
+    case 8: PA_TILE_VARIANTS(8) break;
+    case 16: PA_TILE_VARIANTS(16) break;
+    case 32: PA_TILE_VARIANTS(32) break;
     default: return hipErrorInvalidValue;
   }
+#undef PA_TILE_VARIANTS
   return hipGetLastError();
 }
 

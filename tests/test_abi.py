@@ -89,8 +89,8 @@ def decode_ext(lib, window=0, alibi=None, flags=0, **kw):
 
 @pytest.mark.parametrize("args,code", [
     (dict(window=-1), -2),
-    (dict(window=8, mql=2, qsl=FAKE, T=5, dt=1, D=128), -3),      # no multi-query variant
-    (dict(alibi=FAKE, mql=2, qsl=FAKE, T=5, dt=1, D=128), -3),
+    (dict(window=8, mql=2, qsl=FAKE, T=5, dt=1, D=64), -3),       # tile path: d = 128 only
+    (dict(alibi=FAKE, mql=2, qsl=FAKE, T=5, dt=0, D=128), -3),    # tile path: fp16 only
     (dict(window=8, o=None), -1), (dict(alibi=FAKE, D=32), -3), (dict(window=8, mcl=129), -2),
     (dict(flags=2), -3), (dict(flags=1 << 31), -3),
     (dict(flags=1, H=64, S=65535, T=65535, mcl=2048, mb=128), -2),     # 1-D grid too large

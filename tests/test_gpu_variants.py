@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from paged_kv_cache_40_amd import api
-from workloads import make_config, make_custom_decode
+from workloads import make_config, make_custom_decode, make_custom_mixed
 from paged_harness import (assert_bits_equal, assert_close, host_copy, log, oracle_step,
                            oracle_sub, pick_sequences, run_library, snapshot_for)
 
@@ -153,12 +153,68 @@ def test_full_size_large_batch_window_alibi_sampled():
     log("[ok]")
 
 
-def test_multi_query_variant_rejected():
-    w = make_custom_decode(65, "f16", 2, 128, 16, [40, 50], name="reject")
+# ------------------------------------------- chunked prefill (multi-query tile path) --
+
+CHUNKS = [(0, 2), (0, 64), (17, 65), (300, 130), (1000, 257), (5, 33), (40, 384)]
+CHUNK_CASES = [(1, False), (7, True), (32, False), (33, True), (100, True), (200, False),
+               (5000, True), (0, True)]
+
+
+@pytest.mark.parametrize("block_size", [8, 16, 32])
+@pytest.mark.parametrize("window,use_alibi", CHUNK_CASES)
+def test_chunk_window_alibi(block_size, window, use_alibi):
+    """Chunks of 2..384 queries with short and long priors, mixed with decodes, under windows
+    shorter than one step, at and past a step, shorter and longer than the chunks, and wider
+    than every context; ALiBi alone and with a window."""
+    w = make_custom_mixed(70 + block_size, 3, block_size, CHUNKS, [1, 16, 300, 1025],
+                          name=f"chunks_W{window}_B{block_size}")
+    variant_check(w, window, geometric_slopes(3) if use_alibi else None)
+
+
+def test_chunk_history_before_window_is_never_used():
+    """Chunks whose keys older than the first query's window hold NaN, with the table entries
+    of blocks wholly before it set to -1 (poisoned before any library call; this step's rows,
+    written by each call, all lie inside the window): the tile path must not use them."""
+    H, B, W = 3, 16, 70
+    chunks = [(0, 100), (37, 40), (500, 200), (1000, 300)]
+    w = make_custom_mixed(75, H, B, chunks, [900], name="chunks_window_poisoned")
+    log(f"[case] {w.name} W={W}")
     t = w.device_tensors("cuda")
-    q = torch.zeros(3, 2, 128, dtype=torch.float16, device="cuda")
-    qsl = torch.tensor([0, 2, 3], dtype=torch.int32, device="cuda")
-    with pytest.raises(RuntimeError, match="variant"):
-        api.pa_decode_ext(torch.empty_like(q), q, t["k_pool"], t["v_pool"], t["block_tables"],
-                          t["context_lens"], qsl, max_context_len=50, max_query_len=2,
-                          sliding_window=16)
+    bt = t["block_tables"].cpu().numpy()
+    qsl = w.q_start_loc()
+    blks, slots = [], []
+    for s, L in enumerate(w.context_lens):
+        n = int(qsl[s + 1] - qsl[s])
+        lo = max(0, int(L) - n - W + 1)       # the first query's window start
+        j = np.arange(lo)
+        blks.append(bt[s, j // B])
+        slots.append(j % B)
+        bt[s, :lo // B] = -1
+    blks = torch.from_numpy(np.concatenate(blks).astype(np.int64)).cuda()
+    slots = torch.from_numpy(np.concatenate(slots).astype(np.int64)).cuda()
+    t["k_pool"][blks, slots] = float("nan")
+    t["v_pool"][blks, slots] = float("nan")
+    t["block_tables"] = torch.from_numpy(bt).cuda()
+    h = host_copy(t)
+    slopes = geometric_slopes(H)
+    for al in (None, slopes):
+        out = run_library(w, t, window=W, alibi=al)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out.float()).all()
+        ref, _, _ = oracle_step(w, h, window=W, alibi=al)
+        assert_close(out.cpu().numpy(), ref, "f16", f"poisoned chunk history alibi={al is not None}")
+    log("[ok]")
+
+
+def test_chunk_neutral_variants_bit_identical_to_plain():
+    """On the tile path too, a window at least as long as every context and all-zero slopes
+    reproduce pa_decode bit for bit."""
+    w = make_custom_mixed(76, 4, 16, [(0, 130), (700, 257), (33, 64)], [5, 600], name="chunk_neutral")
+    t = w.device_tensors("cuda")
+    plain = run_library(w, t)                 # each call rewrites the same slots first
+    wide = run_library(w, t, window=int(w.context_lens.max()))
+    zero = run_library(w, t, alibi=np.zeros(4, np.float32))
+    torch.cuda.synchronize()
+    p16 = plain.view(torch.int16)
+    assert torch.equal(wide.view(torch.int16), p16)
+    assert torch.equal(zero.view(torch.int16), p16)
