@@ -320,6 +320,17 @@ def test_chunk_tiles_peaked_scores():
     full_check(w, "q_scale=4")
 
 
+def test_long_contexts():
+    """Long contexts: a 100,000-token decode (about fifty 2048-token partitions merged), a
+    65,537-token one (a one-token last partition) and a 300-query chunk over a 30,000-token
+    prior, next to short ones, against the oracle over every head."""
+    w = make_custom_decode(81, "f16", 4, 128, 16, [100000, 65537, 3, 700], write_one=True,
+                           name="long_decode")
+    full_check(w)
+    w = make_custom_mixed(82, 2, 16, [(30000, 300), (5, 40)], [20000, 9], name="long_chunk")
+    full_check(w)
+
+
 def test_chunk_only_batch():
     """Every sequence is a chunk (no decode units); the tile kernel alone writes the output."""
     w = make_custom_mixed(42, 2, 16, [(64, 64), (5, 128), (0, 256)], [], name="chunks_only")
