@@ -265,6 +265,51 @@ def test_side_stream_and_reused_workspace():
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
 
+def test_graph_capture_replays():
+    """A whole step (slot writes + mixed chunk/decode attention) captured in a HIP graph and
+    replayed several times, with unrelated eager work and synchronisation between replays:
+    every replay equals the eager step bit for bit, and the step equals the oracle.  The
+    library only enqueues kernels (no allocation, no memset), so the step is capturable."""
+    w = make_small(4, seed=1)
+    log(f"[case] graph capture {w.name}")
+    t = w.device_tensors("cuda")
+    h = host_copy(t)
+    need = api.pa_decode_workspace_bytes(w.num_queries, w.num_heads, w.head_dim,
+                                         w.max_context_len)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(t["q"])
+
+    def step():
+        api.pa_write_kv(t["k_pool"], t["v_pool"], t["k_new"], t["v_new"], t["block_tables"],
+                        t["context_lens"], t["write_start_loc"])
+        api.pa_decode_ext(out, t["q"], t["k_pool"], t["v_pool"], t["block_tables"],
+                          t["context_lens"], t["q_start_loc"], max_context_len=w.max_context_len,
+                          max_query_len=w.max_query_len, workspace=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()                                   # eager, on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    ref, _, _ = oracle_step(w, h)
+    assert_close(eager.cpu().numpy(), ref, w.dtype, "eager step")
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    scratch = torch.randn(1 << 20, device="cuda")
+    for i in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
+        scratch.mul_(0.5).add_(1.0)              # unrelated eager work between replays
+        torch.cuda.synchronize()
+    log("[ok] 4 replays bit-identical")
+
+
 # Batch shapes that make the launch pick each context-partition size (the largest of
 # 2048/1024/512/256 tokens that still gives >= 16384 waves), checked on sampled sequences.
 @pytest.mark.parametrize("S,H,lo,hi,B,expect_p", [
