@@ -206,6 +206,27 @@ def _timed(fn, steps: int, warmup: int):
     return wall_ms, float(np.median([a.elapsed_time(b) for a, b in ev]))
 
 
+def _timed_flushed(fn, steps: int, warmup: int, scratch):
+    """Median event time of fn() when a buffer larger than every cache (scratch) is rewritten
+    before each call, so no K/V row of the previous call is still cached."""
+    import numpy as np
+    import torch
+
+    for _ in range(warmup):
+        scratch.add_(1)
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        scratch.add_(1)
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+
 def bench_config(args) -> int:
     """One of the other batches: its whole step (copy-on-write copies, slot writes, attention)."""
     import numpy as np
@@ -238,6 +259,10 @@ def bench_config(args) -> int:
                           sliding_window=args.window, alibi_slopes=slopes)
 
     wall_ms, ev_ms = _timed(step, args.steps, args.warmup)
+    # the same step after a 1 GiB buffer (4x the 256 MB last-level cache) is rewritten
+    scratch = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
+    flushed_ms = _timed_flushed(step, args.steps, args.warmup, scratch)
+    del scratch
     kv = w.kv_bytes_read()
     if args.window:  # K and V rows inside each query row's window, counted once per sequence
         L = w.context_lens.astype(np.int64)
@@ -260,6 +285,8 @@ def bench_config(args) -> int:
                    "alibi": bool(args.alibi),
                    "kv_bytes_logical": kv, "kv_bytes_unique_blocks": unique},
         "event_ms_per_step": round(ev_ms, 4),
+        "flushed_event_ms_per_step": round(flushed_ms, 4),
+        "flushed_GBs": round(kv / (flushed_ms * 1e-3) / 1e9, 2),
         "pct_hbm_peak_logical": round(100 * kv / (wall_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "seq_heads_per_s": round(w.num_seqs * w.num_heads / (wall_ms * 1e-3), 1),
         "kv_memory": kv_memory(w),
