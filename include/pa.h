@@ -119,7 +119,7 @@ size_t pa_decode_workspace_bytes(int32_t num_tokens, int32_t num_heads, int32_t 
  *   (chunked prefill mixed with decodes in one batch, P3 section
  *   "Chunked prefill"), each query attending to positions <= its own.
  * max_context_len, max_query_len: host copies of the maxima over the batch
- *   (grid sizing); max_query_len > 1 requires dtype PA_F16 and head_dim 128.
+ *   (grid sizing); max_query_len > 1 requires dtype PA_F16 (head_dim 64 or 128).
  * workspace: device scratch of at least
  *   pa_decode_workspace_bytes(num_tokens, num_heads, head_dim, max_context_len)
  *   bytes (NULL allowed when that is 0); contents on return are unspecified.

@@ -165,8 +165,8 @@ int pa_decode_ext(void* out, const void* q, const void* k_pool, const void* v_po
               ((max_context_len + pa::kMinPartition - 1) / pa::kMinPartition) >= (int64_t{1} << 24))
     return PA_ERR_SHAPE;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PA_ERR_NULL;
-  // the multi-query tile path is built for fp16 with head_dim 128
-  if (max_query_len > 1 && (dtype != PA_F16 || head_dim != 128)) return PA_ERR_UNSUPPORTED;
+  // the multi-query tile path is built for fp16 (head_dim 64 or 128, as everywhere)
+  if (max_query_len > 1 && dtype != PA_F16) return PA_ERR_UNSUPPORTED;
   if (max_query_len > 1 && (max_query_len + 63) / 64 > 65535) return PA_ERR_SHAPE;
   const size_t need = pa::decode_workspace_bytes(num_tokens, num_heads, head_dim, max_context_len);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_WORKSPACE;

@@ -68,14 +68,25 @@ namespace {
 
 constexpr int kTileQ = 128;       // queries per workgroup (4 waves x 2 column tiles)
 constexpr int kStep = 32;         // keys per step
-constexpr int kD = 128;           // head dim of the tile path
-constexpr float kSqrtD = 11.313708498984761f;  // sqrt(kD)
-constexpr int kKRow = kD + 16;    // K row stride in LDS (halves): 288 B; the 16-byte operand reads
-                                  // run at the full LDS rate with it (272 B measured half rate)
-constexpr int kVRow = kD + 16;    // V row stride in LDS (halves): 288 B, transposing reads spread banks
-constexpr int kKBuf = kStep * kKRow;
-constexpr int kVBuf = kStep * kVRow;
 constexpr int kBufs = 3;          // LDS ring: values of step i, keys of i+1, staging of i+2
+
+// Head-dim dependent geometry (head_dim 64 or 128).
+template <int D>
+struct TileGeom {
+  static constexpr int kSt = D / 32;   // score products per 16-key subtile (32 dims each)
+  static constexpr int kJ = D / 16;    // value products per 32-key group (16 dims each)
+  // LDS row strides (halves): D + 16, i.e. 288 B for D = 128, on which the 16-byte K operand
+  // reads run at the full LDS rate (272 B measured half rate) and the transposing V reads too
+  static constexpr int kKRow = D + 16;
+  static constexpr int kVRow = D + 16;
+  static constexpr int kKBuf = kStep * kKRow;
+  static constexpr int kVBuf = kStep * kVRow;
+  static constexpr int kChunks = D / 8;                // 16-byte chunks per head row
+  static constexpr int kRowsPerLoad = 64 / kChunks;    // rows of one wave load: 4 or 8
+  static constexpr int kLoads = 8 / kRowsPerLoad;      // loads per wave, step and matrix: 2 or 1
+  static constexpr float kSqrtD = D == 128 ? 11.313708498984761f : 8.0f;
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+};
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef __fp16 lds_f16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
@@ -115,9 +126,12 @@ __device__ __forceinline__ f32x4v mfma16(const f16x8& a, const f16x8& b, const f
 #define PA_TILE_OCCUPANCY
 #endif
 
-template <int BS, bool kWindow, bool kAlibi>
+template <int D, int BS, bool kWindow, bool kAlibi>
 __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(TileArgs a) {
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
+  using G = TileGeom<D>;
+  constexpr int kD = D;
+  constexpr int kKRow = G::kKRow, kVRow = G::kVRow, kKBuf = G::kKBuf, kVBuf = G::kVBuf;
   constexpr int kTab = kStep / BS;  // blocks spanned by one step
   __shared__ __attribute__((aligned(16))) f16 lds_k_[kBufs * kKBuf];
   __shared__ __attribute__((aligned(16))) f16 lds_v_[kBufs * kVBuf];
@@ -166,16 +180,16 @@ __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(T
   const int wave_lo_step = W > 0 ? max(0, wave_first_pos - W + 1) / kStep : 0;
   // ALiBi: slope_h * (j - p) is added to q.k_j / sqrt(d); in the raw units of the scores here
   // (q.k) that is slope_h * sqrt(d) * (j - p).
-  const float slope_sd = kAlibi ? a.alibi[h] * kSqrtD : 0.f;
+  const float slope_sd = kAlibi ? a.alibi[h] * G::kSqrtD : 0.f;
 
-  // Q^T operands: lane (lg, lr) holds dims 8*lg + 32*st .. +7 of its query, st = 0..3
-  f16x8 qop[2][4];
+  // Q^T operands: lane (lg, lr) holds dims 8*lg + 32*st .. +7 of its query, st < D/32
+  f16x8 qop[2][G::kSt];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     const f16* qp = static_cast<const f16*>(a.q) +
                     (static_cast<int64_t>(q_first + min(q[qt], n - 1)) * a.num_heads + h) * kD;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
+    for (int st = 0; st < G::kSt; ++st) {
       u32x4 v = ld16(qp + 8 * lg + 32 * st);
       if (q[qt] >= n) v = u32x4{0, 0, 0, 0};
       qop[qt][st] = __builtin_bit_cast(f16x8, v);
@@ -188,19 +202,22 @@ __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(T
   const int32_t* btrow = a.block_tables + static_cast<int64_t>(s) * a.max_blocks;
   const int last_blk = (ctx - 1) / BS;
 
-  // Staging: wave ws stages rows 8*ws + 4*r + l/16 (r = 0, 1) of each step, 16-byte chunk l%16,
-  // so the four rows of one load instruction, and both of its instructions, lie in one block
-  // (block sizes are multiples of 8): the block id is wave-uniform and the pool address is a
-  // scalar block base plus a fixed per-lane offset.
+  // Staging: wave ws stages the 8 rows 8*ws .. 8*ws+7 of each step: load r covers rows
+  // 8*ws + R*r + l/C (R = 64/C rows, C = D/8 16-byte chunks per row), chunk l%C.  The 8 rows
+  // lie in one block (block sizes are multiples of 8), so the block id is wave-uniform and the
+  // pool address is a scalar block base plus a fixed per-lane offset.
+  constexpr int kC = G::kChunks, kR = G::kRowsPerLoad, kL = G::kLoads;
   const int ws = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int srow = 8 * ws + (l >> 4);  // this lane's first staged row
-  const int schunk = l & 15;
+  const int srow = 8 * ws + l / kC;  // this lane's first staged row
+  const int schunk = l % kC;
   const int64_t block_elems = static_cast<int64_t>(BS) * row_stride;
-  const uint32_t toff0 = static_cast<uint32_t>(((srow % BS) * row_stride + 8 * schunk) * 2);
-  const uint32_t toff1 = static_cast<uint32_t>((((srow + 4) % BS) * row_stride + 8 * schunk) * 2);
+  uint32_t toff[kL];
+#pragma unroll
+  for (int r = 0; r < kL; ++r)
+    toff[r] = static_cast<uint32_t>((((srow + kR * r) % BS) * row_stride + 8 * schunk) * 2);
   const char* kpool_b = reinterpret_cast<const char*>(kpool);
   const char* vpool_b = reinterpret_cast<const char*>(vpool);
-  u32x4 k_reg[2], v_reg[2];
+  u32x4 k_reg[kL], v_reg[kL];
   // block id of this wave's rows in `step` (clamped to the last used block; invalid ids
   // read block 0, so every address stays inside the pool)
   const uint32_t nblk32 =
@@ -214,19 +231,20 @@ __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(T
     const int64_t boff = static_cast<int64_t>(blk) * block_elems * 2;
     const char* kb = kpool_b + boff;
     const char* vb = vpool_b + boff;
-    k_reg[0] = ld16(kb + toff0);
-    v_reg[0] = ld16(vb + toff0);
-    k_reg[1] = ld16(kb + toff1);
-    v_reg[1] = ld16(vb + toff1);
+#pragma unroll
+    for (int r = 0; r < kL; ++r) {
+      k_reg[r] = ld16(kb + toff[r]);
+      v_reg[r] = ld16(vb + toff[r]);
+    }
     if (step * kStep + kStep > ctx) {  // the step holding the context's end (wave-uniform)
 #pragma unroll
-      for (int r = 0; r < 2; ++r)
-        if (step * kStep + srow + 4 * r >= ctx) v_reg[r] = u32x4{0, 0, 0, 0};
+      for (int r = 0; r < kL; ++r)
+        if (step * kStep + srow + kR * r >= ctx) v_reg[r] = u32x4{0, 0, 0, 0};
     }
     if (step * kStep < wg_key_lo) {  // the step holding the window's start: older slots may
 #pragma unroll                       // hold anything (their blocks may even be released)
-      for (int r = 0; r < 2; ++r)
-        if (step * kStep + srow + 4 * r < wg_key_lo) v_reg[r] = u32x4{0, 0, 0, 0};
+      for (int r = 0; r < kL; ++r)
+        if (step * kStep + srow + kR * r < wg_key_lo) v_reg[r] = u32x4{0, 0, 0, 0};
     }
   };
   const int kst_off = srow * kKRow + 8 * schunk;
@@ -234,10 +252,11 @@ __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(T
   auto stage = [&](int buf) {
     lf16* kd = lds_k + buf * kKBuf + kst_off;
     lf16* vd = lds_v + buf * kVBuf + vst_off;
-    *(lu32x4*)(kd) = k_reg[0];
-    *(lu32x4*)(vd) = v_reg[0];
-    *(lu32x4*)(kd + 4 * kKRow) = k_reg[1];
-    *(lu32x4*)(vd + 4 * kVRow) = v_reg[1];
+#pragma unroll
+    for (int r = 0; r < kL; ++r) {
+      *(lu32x4*)(kd + kR * r * kKRow) = k_reg[r];
+      *(lu32x4*)(vd + kR * r * kVRow) = v_reg[r];
+    }
   };
 
   // Scores stay in raw units (q.k); c = log2(e)/sqrt(d) is folded into one FMA with the
@@ -246,13 +265,13 @@ __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(T
   const float tau = 8.0f / c;           // reference margin, 2^8 in p
   float m[2] = {-INFINITY, -INFINITY};  // running reference (raw units) per query tile
   float mc[2] = {0.f, 0.f};             // m*c, 0 while m is still -inf
-  f32x4v acc[2][8];
+  f32x4v acc[2][G::kJ];
   f32x4v den[2];                        // O^T row of a ones "dimension": sum of P (row 0)
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     den[qt] = f32x4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[qt][j] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < G::kJ; ++j) acc[qt][j] = f32x4v{0.f, 0.f, 0.f, 0.f};
   }
   // V^T operand of the ones row: lane (g, 0) holds eight ones, every other lane zeros
   f16x8 ones_op;
@@ -286,7 +305,7 @@ __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(T
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
+      for (int st = 0; st < G::kSt; ++st) {
         const f16x8 kop = *(const lf16x8*)(kb + (16 * sub) * kKRow + 32 * st);
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) sc[qt][sub] = mfma16(kop, qop[qt][st], sc[qt][sub]);
@@ -328,7 +347,7 @@ __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(T
         const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2((m[qt] - mn) * c);
         den[qt] *= alpha;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[qt][j] *= alpha;
+        for (int j = 0; j < G::kJ; ++j) acc[qt][j] *= alpha;
         m[qt] = mn;
         mc[qt] = (mn == -INFINITY) ? 0.f : mn * c;
       }
@@ -351,7 +370,7 @@ __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(T
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) den[qt] = mfma16(ones_op, pop[qt], den[qt]);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < G::kJ; ++j) {
       const f16x4 va = lds_read_tr(vrow0 + 16 * j);
       const f16x4 vb = lds_read_tr(vrow1 + 16 * j);
       const f16x8 vop = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
@@ -422,7 +441,7 @@ __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(T
     f16* op = static_cast<f16*>(a.out) +
               (static_cast<int64_t>(q_first + q[qt]) * a.num_heads + h) * kD;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < G::kJ; ++j) {
       f16x4 o;
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] = static_cast<f16>(acc[qt][j][i] * inv);
@@ -433,24 +452,31 @@ __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(T
 
 hipError_t launch_tile(const TileArgs& a, int head_dim, int block_size, int max_query_len,
                        hipStream_t stream) {
-  if (head_dim != kD) return hipErrorInvalidValue;
+  if (head_dim != 64 && head_dim != 128) return hipErrorInvalidValue;
   const int tiles = (max_query_len + kTileQ - 1) / kTileQ;
   dim3 grid(a.num_heads, tiles, a.num_seqs);
   const bool window = a.window > 0;
   const bool alibi = a.alibi != nullptr;
   auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a); };
-  // (window, ALiBi) pick one of four instantiations per block size
-#define PA_TILE_VARIANTS(B_)                                                  \
-  if (window && alibi) go(tile_attention_kernel<B_, true, true>);             \
-  else if (window) go(tile_attention_kernel<B_, true, false>);                \
-  else if (alibi) go(tile_attention_kernel<B_, false, true>);                 \
-  else go(tile_attention_kernel<B_, false, false>);
-  switch (block_size) {
-    case 8: PA_TILE_VARIANTS(8) break;
-    case 16: PA_TILE_VARIANTS(16) break;
-    case 32: PA_TILE_VARIANTS(32) break;
-    default: return hipErrorInvalidValue;
+  // (head_dim, block size, window, ALiBi) pick one instantiation
+#define PA_TILE_VARIANTS(D_, B_)                                                   \
+  if (window && alibi) go(tile_attention_kernel<D_, B_, true, true>);              \
+  else if (window) go(tile_attention_kernel<D_, B_, true, false>);                 \
+  else if (alibi) go(tile_attention_kernel<D_, B_, false, true>);                  \
+  else go(tile_attention_kernel<D_, B_, false, false>);
+#define PA_TILE_BLOCKS(D_)                                                         \
+  switch (block_size) {                                                            \
+    case 8: PA_TILE_VARIANTS(D_, 8) break;                                         \
+    case 16: PA_TILE_VARIANTS(D_, 16) break;                                       \
+    case 32: PA_TILE_VARIANTS(D_, 32) break;                                       \
+    default: return hipErrorInvalidValue;                                          \
   }
+  if (head_dim == 128) {
+    PA_TILE_BLOCKS(128)
+  } else {
+    PA_TILE_BLOCKS(64)
+  }
+#undef PA_TILE_BLOCKS
 #undef PA_TILE_VARIANTS
   return hipGetLastError();
 }

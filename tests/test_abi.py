@@ -89,7 +89,7 @@ def decode_ext(lib, window=0, alibi=None, flags=0, **kw):
 
 @pytest.mark.parametrize("args,code", [
     (dict(window=-1), -2),
-    (dict(window=8, mql=2, qsl=FAKE, T=5, dt=1, D=64), -3),       # tile path: d = 128 only
+    (dict(window=8, mql=2, qsl=FAKE, T=5, dt=0, D=64), -3),       # tile path: fp16 only
     (dict(alibi=FAKE, mql=2, qsl=FAKE, T=5, dt=0, D=128), -3),    # tile path: fp16 only
     (dict(window=8, o=None), -1), (dict(alibi=FAKE, D=32), -3), (dict(window=8, mcl=129), -2),
     (dict(flags=2), -3), (dict(flags=1 << 31), -3),

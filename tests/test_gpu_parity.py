@@ -359,6 +359,16 @@ def test_chunk_tiles_multi_tile(B):
     full_check(w)
 
 
+@pytest.mark.parametrize("B", [8, 16, 32])
+def test_chunk_tiles_head_dim_64(B):
+    """The tile path at head_dim 64: chunks of 2..511 queries over short and long priors
+    (one to four 128-query tiles, contexts ending mid-block), mixed with decodes."""
+    chunks = [(0, 2), (17, 65), (300, 130), (1000, 257), (5, 511), (40, 384)]
+    w = make_custom_mixed(90 + B, 3, B, chunks, [1, 300, 1025], name=f"chunks_d64_B{B}",
+                          head_dim=64)
+    full_check(w)
+
+
 def test_chunk_tiles_peaked_scores():
     w = make_custom_mixed(41, 3, 16, [(200, 100), (0, 70)], [50], name="chunks_peaked",
                           q_scale=4.0)

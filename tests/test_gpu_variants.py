@@ -171,6 +171,13 @@ def test_chunk_window_alibi(block_size, window, use_alibi):
     variant_check(w, window, geometric_slopes(3) if use_alibi else None)
 
 
+@pytest.mark.parametrize("window,use_alibi", [(7, True), (100, False), (0, True)])
+def test_chunk_window_alibi_head_dim_64(window, use_alibi):
+    w = make_custom_mixed(78, 3, 16, CHUNKS, [1, 300], name=f"chunks_d64_W{window}",
+                          head_dim=64)
+    variant_check(w, window, geometric_slopes(3) if use_alibi else None)
+
+
 def test_chunk_history_before_window_is_never_used():
     """Chunks whose keys older than the first query's window hold NaN, with the table entries
     of blocks wholly before it set to -1 (poisoned before any library call; this step's rows,

@@ -345,7 +345,7 @@ def make_custom_decode(seed, dtype, num_heads, head_dim, block_size, lens, num_b
 
 
 def make_custom_mixed(seed, num_heads, block_size, chunks, decode_lens, name="custom_mixed",
-                      q_scale=1.0):
+                      q_scale=1.0, head_dim=128):
     """Chunks (prior tokens, new tokens) attending causally, plus single-token decodes, in one
     batch (order shuffled); every new token is also appended this step."""
     rng = np.random.default_rng(seed)
@@ -358,7 +358,7 @@ def make_custom_mixed(seed, num_heads, block_size, chunks, decode_lens, name="cu
     nb = max(need + 2, _cdiv(5 * need, 4))
     bt = _tables_from_permutation(rng, lens, block_size, nb)
     filled = _filled_from_tables(bt, lens - qlens, block_size, nb)
-    return Workload(name=name, seed=seed, dtype="f16", num_heads=num_heads, head_dim=128,
+    return Workload(name=name, seed=seed, dtype="f16", num_heads=num_heads, head_dim=head_dim,
                     block_size=block_size, num_blocks=nb, context_lens=lens, query_lens=qlens,
                     write_lens=qlens.copy(), block_tables=bt, filled_before=filled,
                     q_scale=q_scale)
