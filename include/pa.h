@@ -44,7 +44,14 @@
  *     entries of used blocks in [0, num_blocks), copy destinations distinct and
  *     never a source.  The kernels clamp or skip anything that would address
  *     memory outside the buffers described here, so a violated precondition
- *     gives unspecified values, never an out-of-bounds access.
+ *     gives unspecified values, never an out-of-bounds access: attention
+ *     clamps context lengths to the table width (single-query sequences
+ *     also to max_context_len), skips a sequence whose length is below 1
+ *     or below its query count and reads block 0 in place of an
+ *     out-of-range block id; writes skip slots at negative or out-of-table
+ *     positions and in out-of-range blocks; copies skip pairs with an
+ *     out-of-range id.  Out-of-range ids and lengths of one sequence
+ *     therefore change only that sequence's outputs and its own blocks.
  */
 #ifndef PAGED_KV_PA_H
 #define PAGED_KV_PA_H

@@ -38,9 +38,9 @@
 //   partition merges the partials and writes out.
 //
 // All pool offsets are 64-bit.  Context lengths are clamped to the table
-// width and to the host bound, and block ids outside [0, num_blocks) are
-// replaced by block 0, so malformed device data cannot address memory
-// outside the pools or the workspace.
+// width and to the host bound (a sequence with no tokens is skipped), and
+// block ids outside [0, num_blocks) are replaced by block 0, so malformed
+// device data cannot address memory outside the pools or the workspace.
 
 #include <math.h>
 
@@ -167,6 +167,7 @@ void decode_partition_kernel(DecodeArgs a) {
   }
   if (qrow < 0 || qrow >= a.num_tokens) return;
   const int ctx = min(a.context_lens[s], min(a.max_blocks * BS, a.max_context_len));
+  if (ctx <= 0) return;  // malformed length: nothing to read (the merge pass skips it too)
   // with a sliding window the query (position ctx-1) sees tokens lo .. ctx-1; partitions
   // start at the window's first block, so older blocks are never read
   const int lo = a.window > 0 ? max(0, ctx - a.window) : 0;
