@@ -225,6 +225,86 @@ int pa_swap_blocks(void* dev_k, void* dev_v, int64_t num_dev_blocks,
                    int32_t num_heads, int32_t head_dim, int32_t block_size,
                    int32_t dtype, void* stream);
 
+/*
+ * Precondition checks — the device-resident contents every call above takes on
+ * trust (Errors, under the conventions), checked on the device for the same
+ * arguments a call would get.  For debugging and for callers that build tables
+ * from untrusted input; a serving loop built on the block manager does not
+ * need them.  What is checked follows from the addressing the calls implement
+ * (P1 sec. 4, the addressing sentence after the attention equation; P1 sec. 5,
+ * Fig. 7: token j of sequence s sits in block block_tables[s][j / block_size],
+ * slot j % block_size) and from copy-on-write (P2 pseudocode: copy_on_write
+ * gives the writer its own block; P1 sec. 6, Fig. 9).
+ *
+ * error_word: ONE uint64 in device memory, owned by the caller.  Each check
+ *   first sets it to PA_CHECK_OK (all ones), then every violation found lowers
+ *   it by atomic minimum to (kind << 32) | index, index being the sequence (or
+ *   pair) number.  On completion the word holds the smallest kind found and,
+ *   for that kind, the smallest index: the same inputs always give the same
+ *   word.  Read it after synchronising the stream.
+ * workspace (pa_check_write, pa_check_pairs): device scratch of at least
+ *   pa_check_workspace_bytes(n) bytes, n = num_blocks * block_size (write) or
+ *   num_dst_blocks (pairs); contents on return unspecified.
+ * Host arguments are validated as for the calls themselves (negative status,
+ * nothing launched).  The checks read only inside the arrays described, so
+ * they are safe on any contents.  They enqueue on `stream` and return.
+ */
+#define PA_CHECK_OK 0xFFFFFFFFFFFFFFFFull
+
+typedef enum {
+  PA_CHECK_START_LOC = 1,       /* start locations not 0-based, decreasing, or last > num_tokens */
+  PA_CHECK_QUERY_COUNT = 2,     /* attention: n_s < 1 or n_s > max_query_len                      */
+  PA_CHECK_CONTEXT_LEN = 3,     /* context_lens[s] < n_s, > max_blocks_per_seq*block_size, or
+                                   (attention) > max_context_len                                  */
+  PA_CHECK_BLOCK_ID = 4,        /* a table entry the call uses is outside [0, num_blocks)         */
+  PA_CHECK_SLOT_REUSED = 5,     /* write: tokens of this sequence share a slot with another token */
+  PA_CHECK_PAIR_ID = 6,         /* pairs: src or dst outside its pool                             */
+  PA_CHECK_DEST_REUSED = 7,     /* pairs: this pair's destination is another pair's destination   */
+  PA_CHECK_DEST_IS_SOURCE = 8   /* pairs in one pool: this pair's source is some pair's destination */
+} pa_check_kind;
+
+/* pa_check_workspace_bytes — scratch for n marks (two bits each); 0 when n <= 0. */
+size_t pa_check_workspace_bytes(int64_t num_marks);
+
+/*
+ * pa_check_attention — the device preconditions of pa_decode / pa_decode_ext
+ * with these arguments: start locations, 1 <= n_s <= max_query_len,
+ * n_s <= context_lens[s] <= min(max_blocks_per_seq*block_size, max_context_len),
+ * and every table entry whose block holds a key some query of s attends to
+ * (with sliding_window W > 0, keys from position context_lens[s]-n_s-W+1 on)
+ * in [0, num_blocks).
+ */
+int pa_check_attention(uint64_t* error_word, int64_t num_blocks,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* context_lens, const int32_t* q_start_loc,
+                       int32_t num_seqs, int32_t num_tokens,
+                       int32_t max_context_len, int32_t max_query_len,
+                       int32_t block_size, int32_t sliding_window, void* stream);
+
+/*
+ * pa_check_write — the device preconditions of pa_write_kv: start locations
+ * (n_s = 0 allowed), n_s <= context_lens[s] <= max_blocks_per_seq*block_size,
+ * the table entries of the written positions in [0, num_blocks), and no two
+ * written tokens in one slot (every writer of a shared slot is reported).
+ */
+int pa_check_write(uint64_t* error_word, void* workspace, size_t workspace_bytes,
+                   int64_t num_blocks, const int32_t* block_tables,
+                   int32_t max_blocks_per_seq, const int32_t* context_lens,
+                   const int32_t* write_start_loc, int32_t num_seqs, int32_t num_tokens,
+                   int32_t block_size, void* stream);
+
+/*
+ * pa_check_pairs — the device preconditions of pa_copy_blocks (same_pool = 1,
+ * num_src_blocks == num_dst_blocks == num_blocks) or pa_swap_blocks
+ * (same_pool = 0; source and destination pools sized separately): ids inside
+ * their pools, destinations distinct (every pair of a shared destination is
+ * reported) and, inside one pool, no source that is also a destination.
+ */
+int pa_check_pairs(uint64_t* error_word, void* workspace, size_t workspace_bytes,
+                   int64_t num_src_blocks, int64_t num_dst_blocks,
+                   const int32_t* block_pairs, int32_t num_pairs, int32_t same_pool,
+                   void* stream);
+
 /* pa_strerror — static text for a pa_status value (never NULL). */
 const char* pa_strerror(int status);
 

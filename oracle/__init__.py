@@ -13,7 +13,10 @@ reordering beyond what the definitions state):
   * kv_ops.py    — the slot write of newly generated tokens, the
     copy-on-write whole-block copy and the block swap between the device
     pool and a host swap pool;
-  * sizes.py     — the KV-cache byte formulas.
+  * sizes.py     — the KV-cache byte formulas;
+  * preconditions.py — the conditions the device-resident inputs (tables,
+    lengths, start locations, block pairs) must meet, and the first one a
+    batch breaks.
 
 Sources (cited by key in every file):
   P1 = "Efficient Memory Management for Large Language Model Serving with
@@ -31,3 +34,4 @@ the figures the pages print); see tests/test_oracle_*.py.
 from .attention import gather_context, attend, paged_attention, paged_attention_seq  # noqa: F401
 from .kv_ops import write_kv, copy_blocks, swap_blocks  # noqa: F401
 from .sizes import kv_bytes_per_token, block_bytes  # noqa: F401
+from . import preconditions  # noqa: F401

@@ -15,6 +15,10 @@ PA_F32, PA_F16 = 0, 1
 PA_OK = 0
 PA_SWAP_OUT, PA_SWAP_IN = 0, 1
 PA_DECODE_SHARED_BLOCKS = 1
+PA_CHECK_OK = 0xFFFFFFFFFFFFFFFF
+# pa_check_kind values
+CHECK_KINDS = {1: "START_LOC", 2: "QUERY_COUNT", 3: "CONTEXT_LEN", 4: "BLOCK_ID",
+               5: "SLOT_REUSED", 6: "PAIR_ID", 7: "DEST_REUSED", 8: "DEST_IS_SOURCE"}
 
 _c_int, _c_i32, _c_i64, _c_size = ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 _vp = ctypes.c_void_p
@@ -33,6 +37,12 @@ SIGNATURES = {
                                 _vp]),
     "pa_swap_blocks": (_c_int, [_vp, _vp, _c_i64, _vp, _vp, _c_i64, _vp, _c_i32, _c_i32, _c_i32,
                                 _c_i32, _c_i32, _c_i32, _vp]),
+    "pa_check_workspace_bytes": (_c_size, [_c_i64]),
+    "pa_check_attention": (_c_int, [_vp, _c_i64, _vp, _c_i32, _vp, _vp, _c_i32, _c_i32, _c_i32,
+                                    _c_i32, _c_i32, _c_i32, _vp]),
+    "pa_check_write": (_c_int, [_vp, _vp, _c_size, _c_i64, _vp, _c_i32, _vp, _vp, _c_i32, _c_i32,
+                                _c_i32, _vp]),
+    "pa_check_pairs": (_c_int, [_vp, _vp, _c_size, _c_i64, _c_i64, _vp, _c_i32, _c_i32, _vp]),
     "pa_strerror": (ctypes.c_char_p, [_c_int]),
 }
 

@@ -4,17 +4,44 @@ Argument marshalling only: shapes and dtypes are read from the tensors, device
 pointers and the current HIP stream are passed through ctypes, and every step
 of the computation runs in the HIP kernels of libpagedkv.so.  A nonzero status
 raises RuntimeError with the library's message.
+
+Debug mode (environment variable PA_DEBUG=1 at import, or set_debug(True)):
+every call first runs the library's device-side precondition check for its
+arguments (pa_check_attention / pa_check_write / pa_check_pairs), waits for it,
+and raises PreconditionError instead of launching when a precondition fails.
 """
 
 from __future__ import annotations
 
-from typing import Optional
+import os
+from typing import Optional, Tuple
 
 import torch
 
 from . import _lib
 
 _DTYPES = {torch.float32: _lib.PA_F32, torch.float16: _lib.PA_F16}
+
+_debug = os.environ.get("PA_DEBUG", "") not in ("", "0")
+
+
+def set_debug(enabled: bool) -> None:
+    """Check the device preconditions before every call (see the module docstring)."""
+    global _debug
+    _debug = bool(enabled)
+
+
+def debug_enabled() -> bool:
+    return _debug
+
+
+class PreconditionError(RuntimeError):
+    """A device-side precondition of a call does not hold: kind (a pa_check_kind name) and
+    the lowest sequence or pair index showing it."""
+
+    def __init__(self, what: str, kind: str, index: int):
+        super().__init__(f"{what}: precondition {kind} violated at index {index}")
+        self.kind, self.index = kind, index
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -51,6 +78,85 @@ def _check_index(t: Optional[torch.Tensor], name: str, n: Optional[int] = None):
         _require(t.shape[0] == n, f"{name} must have {n} rows")
 
 
+def _new_word(device) -> torch.Tensor:
+    return torch.empty(1, dtype=torch.int64, device=device)
+
+
+def _read_word(word: torch.Tensor, stream) -> Optional[Tuple[str, int]]:
+    """Wait for the check on `stream`, then decode the word: None or (kind name, index)."""
+    (torch.cuda.current_stream() if stream is None else stream).synchronize()
+    w = int(word.item()) & 0xFFFFFFFFFFFFFFFF
+    if w == _lib.PA_CHECK_OK:
+        return None
+    return _lib.CHECK_KINDS.get(w >> 32, f"kind {w >> 32}"), w & 0xFFFFFFFF
+
+
+def pa_check_workspace_bytes(num_marks: int) -> int:
+    return int(_lib.load().pa_check_workspace_bytes(int(num_marks)))
+
+
+def pa_check_attention(k_pool, block_tables, context_lens, q_start_loc=None, num_tokens=None,
+                       max_context_len: Optional[int] = None, max_query_len: int = 1,
+                       sliding_window: int = 0, stream=None) -> Optional[Tuple[str, int]]:
+    """Device preconditions of pa_decode(_ext) with these arguments.  Waits for the check and
+    returns None when they hold, else (kind, lowest sequence index)."""
+    nb, bs = k_pool.shape[0], k_pool.shape[1]
+    S = context_lens.shape[0]
+    _check_index(block_tables, "block_tables", S)
+    _check_index(context_lens, "context_lens")
+    _check_index(q_start_loc, "q_start_loc", S + 1)
+    T = S if num_tokens is None else int(num_tokens)
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item())
+    word = _new_word(context_lens.device)
+    st = _lib.load().pa_check_attention(
+        _ptr(word), nb, _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        _ptr(q_start_loc), S, T, int(max_context_len), int(max_query_len), bs,
+        int(sliding_window), _stream(stream))
+    _lib.check(st, "pa_check_attention")
+    return _read_word(word, stream)
+
+
+def pa_check_write(k_pool, block_tables, context_lens, write_start_loc=None, num_tokens=None,
+                   stream=None) -> Optional[Tuple[str, int]]:
+    """Device preconditions of pa_write_kv with these arguments (see pa_check_attention)."""
+    nb, bs = k_pool.shape[0], k_pool.shape[1]
+    S = context_lens.shape[0]
+    _check_index(block_tables, "block_tables", S)
+    _check_index(context_lens, "context_lens")
+    _check_index(write_start_loc, "write_start_loc", S + 1)
+    T = S if num_tokens is None else int(num_tokens)
+    need = pa_check_workspace_bytes(nb * bs)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=context_lens.device)
+    word = _new_word(context_lens.device)
+    st = _lib.load().pa_check_write(
+        _ptr(word), _ptr(ws), need, nb, _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), _ptr(write_start_loc), S, T, bs, _stream(stream))
+    _lib.check(st, "pa_check_write")
+    return _read_word(word, stream)
+
+
+def pa_check_pairs(block_pairs, num_src_blocks: int, num_dst_blocks: int, same_pool: bool,
+                   stream=None) -> Optional[Tuple[str, int]]:
+    """Device preconditions of pa_copy_blocks (same_pool) or pa_swap_blocks; returns None or
+    (kind, lowest pair index)."""
+    _check_index(block_pairs, "block_pairs")
+    _require(block_pairs.dim() == 2 and block_pairs.shape[1] == 2, "block_pairs must be [n][2]")
+    need = pa_check_workspace_bytes(num_dst_blocks)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=block_pairs.device)
+    word = _new_word(block_pairs.device)
+    st = _lib.load().pa_check_pairs(_ptr(word), _ptr(ws), need, int(num_src_blocks),
+                                    int(num_dst_blocks), _ptr(block_pairs),
+                                    block_pairs.shape[0], 1 if same_pool else 0, _stream(stream))
+    _lib.check(st, "pa_check_pairs")
+    return _read_word(word, stream)
+
+
+def _raise_if(found, what: str) -> None:
+    if found is not None:
+        raise PreconditionError(what, found[0], found[1])
+
+
 def pa_decode_workspace_bytes(num_tokens: int, num_heads: int, head_dim: int,
                               max_context_len: int) -> int:
     return int(_lib.load().pa_decode_workspace_bytes(num_tokens, num_heads, head_dim,
@@ -68,6 +174,9 @@ def pa_write_kv(k_pool, v_pool, k_new, v_new, block_tables, context_lens,
     _require(k_new.shape == v_new.shape == (T, h, d), "k_new / v_new must be [T][H][d]")
     _require(k_new.dtype == v_new.dtype == k_pool.dtype, "k_new / v_new dtype must match the pool")
     _require(k_new.is_contiguous() and v_new.is_contiguous(), "k_new / v_new must be contiguous")
+    if _debug:
+        _raise_if(pa_check_write(k_pool, block_tables, context_lens, write_start_loc, T, stream),
+                  "pa_write_kv")
     st = _lib.load().pa_write_kv(
         _ptr(k_pool), _ptr(v_pool), nb, _ptr(k_new), _ptr(v_new), _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), _ptr(write_start_loc), S, T, h, d, bs, dt,
@@ -79,6 +188,8 @@ def pa_copy_blocks(k_pool, v_pool, block_pairs, stream=None) -> None:
     nb, bs, h, d, dt = _check_pool(k_pool, v_pool)
     _check_index(block_pairs, "block_pairs")
     _require(block_pairs.dim() == 2 and block_pairs.shape[1] == 2, "block_pairs must be [n][2]")
+    if _debug:
+        _raise_if(pa_check_pairs(block_pairs, nb, nb, True, stream), "pa_copy_blocks")
     st = _lib.load().pa_copy_blocks(_ptr(k_pool), _ptr(v_pool), nb, _ptr(block_pairs),
                                     block_pairs.shape[0], h, d, bs, dt, _stream(stream))
     _lib.check(st, "pa_copy_blocks")
@@ -101,6 +212,10 @@ def pa_swap_blocks(k_pool, v_pool, host_k, host_v, block_pairs, direction: str,
     _require(not host_k.is_cuda and not host_v.is_cuda and host_k.is_contiguous() and
              host_v.is_contiguous(), "host pools must be contiguous CPU tensors")
     _require(host_k.is_pinned() and host_v.is_pinned(), "host pools must be pinned memory")
+    if _debug:
+        nh = host_k.shape[0]
+        src_n, dst_n = (nb, nh) if direction == "out" else (nh, nb)
+        _raise_if(pa_check_pairs(block_pairs, src_n, dst_n, False, stream), "pa_swap_blocks")
     st = _lib.load().pa_swap_blocks(
         _ptr(k_pool), _ptr(v_pool), nb, _ptr(host_k), _ptr(host_v), host_k.shape[0],
         _ptr(block_pairs), block_pairs.shape[0],
@@ -149,6 +264,10 @@ def pa_decode_ext(out, q, k_pool, v_pool, block_tables, context_lens, q_start_lo
         _require(alibi_slopes.dtype == torch.float32 and alibi_slopes.is_cuda and
                  alibi_slopes.is_contiguous() and alibi_slopes.numel() == h,
                  "alibi_slopes must be a contiguous float32 GPU tensor [num_heads]")
+    if _debug:
+        _raise_if(pa_check_attention(k_pool, block_tables, context_lens, q_start_loc, T,
+                                     max_context_len, max_query_len, sliding_window, stream),
+                  "pa_decode")
     st = _lib.load().pa_decode_ext(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), nb, _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), _ptr(q_start_loc), S, T, int(max_context_len),

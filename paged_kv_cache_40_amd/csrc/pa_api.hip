@@ -57,7 +57,7 @@ const char* pa_strerror(int status) {
     case PA_ERR_NULL: return "a required pointer argument is NULL";
     case PA_ERR_SHAPE: return "sizes out of range or inconsistent";
     case PA_ERR_UNSUPPORTED: return "dtype, head_dim, block_size or variant not supported";
-    case PA_ERR_WORKSPACE: return "workspace missing or smaller than pa_decode_workspace_bytes";
+    case PA_ERR_WORKSPACE: return "workspace missing or smaller than the entry point requires";
     case PA_ERR_LAUNCH: return "kernel launch failed";
     case PA_ERR_HOST_MEMORY: return "host pool is not pinned host memory mapped for the device";
     default: return "unknown status";
@@ -213,6 +213,60 @@ int pa_decode_ext(void* out, const void* q, const void* k_pool, const void* v_po
   ta.window = sliding_window;
   ta.alibi = alibi_slopes;
   return launch_status(pa::launch_tile(ta, head_dim, block_size, max_query_len, st));
+}
+
+size_t pa_check_workspace_bytes(int64_t num_marks) {
+  if (num_marks <= 0) return 0;
+  return static_cast<size_t>(2 * pa::check_mark_words(num_marks) * 4);
+}
+
+int pa_check_attention(uint64_t* error_word, int64_t num_blocks, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens,
+                       const int32_t* q_start_loc, int32_t num_seqs, int32_t num_tokens,
+                       int32_t max_context_len, int32_t max_query_len, int32_t block_size,
+                       int32_t sliding_window, void* stream) {
+  if (num_blocks <= 0 || num_seqs <= 0 || num_tokens <= 0 || max_blocks_per_seq <= 0)
+    return PA_ERR_SHAPE;
+  if (!block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+  if (max_context_len <= 0 || max_query_len <= 0 || sliding_window < 0) return PA_ERR_SHAPE;
+  if (q_start_loc == nullptr && num_tokens != num_seqs) return PA_ERR_SHAPE;
+  if (!error_word || !block_tables || !context_lens) return PA_ERR_NULL;
+  return launch_status(pa::launch_check_attention(
+      error_word, num_blocks, block_tables, max_blocks_per_seq, context_lens, q_start_loc,
+      num_seqs, num_tokens, max_context_len, max_query_len, block_size, sliding_window,
+      static_cast<hipStream_t>(stream)));
+}
+
+int pa_check_write(uint64_t* error_word, void* workspace, size_t workspace_bytes,
+                   int64_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                   const int32_t* context_lens, const int32_t* write_start_loc, int32_t num_seqs,
+                   int32_t num_tokens, int32_t block_size, void* stream) {
+  if (num_blocks <= 0 || num_seqs <= 0 || num_tokens < 0 || max_blocks_per_seq <= 0)
+    return PA_ERR_SHAPE;
+  if (!block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+  if (write_start_loc == nullptr && num_tokens != num_seqs) return PA_ERR_SHAPE;
+  if (num_blocks > INT64_MAX / block_size) return PA_ERR_SHAPE;
+  if (!error_word || !block_tables || !context_lens) return PA_ERR_NULL;
+  if (workspace == nullptr || workspace_bytes < pa_check_workspace_bytes(num_blocks * block_size))
+    return PA_ERR_WORKSPACE;
+  return launch_status(pa::launch_check_write(error_word, workspace, num_blocks, block_tables,
+                                              max_blocks_per_seq, context_lens, write_start_loc,
+                                              num_seqs, num_tokens, block_size,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int pa_check_pairs(uint64_t* error_word, void* workspace, size_t workspace_bytes,
+                   int64_t num_src_blocks, int64_t num_dst_blocks, const int32_t* block_pairs,
+                   int32_t num_pairs, int32_t same_pool, void* stream) {
+  if (num_src_blocks <= 0 || num_dst_blocks <= 0 || num_pairs < 0) return PA_ERR_SHAPE;
+  if (same_pool != 0 && same_pool != 1) return PA_ERR_SHAPE;
+  if (same_pool && num_src_blocks != num_dst_blocks) return PA_ERR_SHAPE;
+  if (!error_word || (num_pairs > 0 && !block_pairs)) return PA_ERR_NULL;
+  if (workspace == nullptr || workspace_bytes < pa_check_workspace_bytes(num_dst_blocks))
+    return PA_ERR_WORKSPACE;
+  return launch_status(pa::launch_check_pairs(error_word, workspace, num_src_blocks,
+                                              num_dst_blocks, block_pairs, num_pairs, same_pool,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

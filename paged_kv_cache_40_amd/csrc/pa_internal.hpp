@@ -80,4 +80,23 @@ hipError_t launch_copy_blocks(void* k_pool, void* v_pool, int64_t num_blocks,
                               const int32_t* block_pairs, int32_t num_pairs, int64_t block_bytes,
                               hipStream_t stream);
 
+// Device-side precondition checks (pa_check.hip).  err: one 64-bit word; workspace: two
+// bitmaps of check_mark_words(n) words each (n = slots for a write, destination blocks for
+// pairs).
+int64_t check_mark_words(int64_t marks);
+hipError_t launch_check_attention(uint64_t* err, int64_t num_blocks, const int32_t* block_tables,
+                                  int32_t max_blocks, const int32_t* context_lens,
+                                  const int32_t* q_start_loc, int32_t num_seqs,
+                                  int32_t num_tokens, int32_t max_context_len,
+                                  int32_t max_query_len, int32_t block_size, int32_t window,
+                                  hipStream_t stream);
+hipError_t launch_check_write(uint64_t* err, void* workspace, int64_t num_blocks,
+                              const int32_t* block_tables, int32_t max_blocks,
+                              const int32_t* context_lens, const int32_t* write_start_loc,
+                              int32_t num_seqs, int32_t num_tokens, int32_t block_size,
+                              hipStream_t stream);
+hipError_t launch_check_pairs(uint64_t* err, void* workspace, int64_t num_src, int64_t num_dst,
+                              const int32_t* pairs, int32_t num_pairs, int32_t same_pool,
+                              hipStream_t stream);
+
 }  // namespace pa

@@ -41,7 +41,8 @@ __global__ __launch_bounds__(kCopyThreads) void write_kv_kernel(
     const int32_t* write_start_loc, int32_t num_seqs, int32_t num_tokens, int64_t row_bytes,
     int32_t block_size) {
   const int t = blockIdx.x;
-  int s = t, first = t, n = 1;
+  int s = t;
+  int64_t first = t, n = 1;  // 64-bit: malformed device values cannot overflow
   if (write_start_loc != nullptr) {
     // largest s with write_start_loc[s] <= t (sequences with no new token are skipped)
     int lo = 0, hi = num_seqs - 1;
@@ -54,8 +55,8 @@ __global__ __launch_bounds__(kCopyThreads) void write_kv_kernel(
     n = write_start_loc[s + 1] - first;
     if (t < first || t - first >= n) return;
   }
-  const int p = context_lens[s] - n + (t - first);
-  if (p < 0 || p >= max_blocks * block_size) return;
+  const int64_t p = context_lens[s] - n + (t - first);
+  if (p < 0 || p >= static_cast<int64_t>(max_blocks) * block_size) return;
   const int blk = block_tables[static_cast<int64_t>(s) * max_blocks + p / block_size];
   if (blk < 0 || blk >= num_blocks) return;
   const int64_t dst = (static_cast<int64_t>(blk) * block_size + p % block_size) * row_bytes;

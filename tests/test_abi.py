@@ -174,3 +174,62 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError):
         _lib.load(str(tmp_path / "missing.so"))
+
+
+def test_check_workspace_bytes(lib):
+    f = lib.pa_check_workspace_bytes
+    assert f(0) == 0 and f(-3) == 0
+    assert f(1) == 8                      # two bitmaps of one 32-bit word
+    assert f(32) == 8 and f(33) == 16
+    assert f(47104 * 16) == 2 * 4 * (47104 * 16 // 32)
+
+
+def check_attention(lib, **kw):
+    a = dict(err=FAKE, nb=64, bt=FAKE, mb=8, cl=FAKE, qsl=None, S=4, T=4, mcl=100, mql=1, B=16,
+             W=0)
+    a.update(kw)
+    return lib.pa_check_attention(a["err"], a["nb"], a["bt"], a["mb"], a["cl"], a["qsl"], a["S"],
+                                  a["T"], a["mcl"], a["mql"], a["B"], a["W"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(err=None), -1), (dict(bt=None), -1), (dict(cl=None), -1),
+    (dict(nb=0), -2), (dict(S=0), -2), (dict(T=0), -2), (dict(mb=0), -2), (dict(mcl=0), -2),
+    (dict(mql=0), -2), (dict(W=-1), -2), (dict(T=5), -2), (dict(B=12), -3),
+])
+def test_check_attention_rejects(lib, kw, code):
+    assert check_attention(lib, **kw) == code
+
+
+def check_write(lib, **kw):
+    a = dict(err=FAKE, ws=FAKE, wsb=1 << 20, nb=64, bt=FAKE, mb=8, cl=FAKE, wsl=None, S=4, T=4,
+             B=16)
+    a.update(kw)
+    return lib.pa_check_write(a["err"], a["ws"], a["wsb"], a["nb"], a["bt"], a["mb"], a["cl"],
+                              a["wsl"], a["S"], a["T"], a["B"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(err=None), -1), (dict(bt=None), -1), (dict(cl=None), -1),
+    (dict(nb=0), -2), (dict(S=0), -2), (dict(T=-1), -2), (dict(T=5), -2), (dict(mb=0), -2),
+    (dict(B=4), -3), (dict(ws=None), -4), (dict(wsb=255), -4),   # 64 x 16 slots need 256 B
+])
+def test_check_write_rejects(lib, kw, code):
+    assert check_write(lib, **kw) == code
+
+
+def check_pairs(lib, **kw):
+    a = dict(err=FAKE, ws=FAKE, wsb=1 << 20, ns=64, nd=64, pairs=FAKE, n=3, same=1)
+    a.update(kw)
+    return lib.pa_check_pairs(a["err"], a["ws"], a["wsb"], a["ns"], a["nd"], a["pairs"], a["n"],
+                              a["same"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(err=None), -1), (dict(pairs=None), -1),
+    (dict(ns=0), -2), (dict(nd=-1), -2), (dict(n=-1), -2), (dict(same=2), -2),
+    (dict(nd=32), -2),                     # one pool needs equal sizes
+    (dict(ws=None), -4), (dict(wsb=15), -4),
+])
+def test_check_pairs_rejects(lib, kw, code):
+    assert check_pairs(lib, **kw) == code

@@ -1,0 +1,190 @@
+"""Pins of oracle.preconditions (CPU).
+
+Each case is a tiny batch built by hand with the verdict written out by hand
+from the definitions (not by running the checker); batches that a block
+manager builds by forks, appends and copy-on-write must pass every check.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import preconditions as pc
+from paged_kv_cache_40_amd.block_manager import BlockManager, tables_to_array
+
+I32 = np.int32
+
+
+def bt(*rows, width=None):
+    w = width or max(len(r) for r in rows)
+    a = np.full((len(rows), w), -1, I32)
+    for i, r in enumerate(rows):
+        a[i, :len(r)] = r
+    return a
+
+
+# a well-formed 3-sequence batch over a 10-block pool, B = 4:
+#   seq 0: 6 tokens (blocks 3, 7), 2 new; seq 1: 4 tokens (block 0), 1 new;
+#   seq 2: 9 tokens (blocks 5, 2, 9), 3 new.  Tables are 4 wide.
+TABLES = bt([3, 7], [0], [5, 2, 9], width=4)
+LENS = np.asarray([6, 4, 9], I32)
+LOC = np.asarray([0, 2, 3, 6], I32)
+NB, B, T = 10, 4, 6
+
+
+def attn(tables=TABLES, lens=LENS, loc=LOC, nb=NB, T=T, mcl=16, mql=3, window=0):
+    return pc.check_attention(tables, lens, loc, nb, B, T, mcl, mql, window)
+
+
+def write(tables=TABLES, lens=LENS, loc=LOC, nb=NB, T=T):
+    return pc.check_write(tables, lens, loc, nb, B, T)
+
+
+def test_well_formed_batch_passes():
+    assert attn() is None
+    assert write() is None
+    # one token per sequence without start locations
+    assert pc.check_attention(TABLES, LENS, None, NB, B, 3, 9, 1) is None
+    assert pc.check_write(TABLES, LENS, None, NB, B, 3) is None
+
+
+@pytest.mark.parametrize("loc,want", [
+    ([1, 2, 3, 6], (pc.START_LOC, 0)),   # not 0-based
+    ([0, 3, 2, 6], (pc.START_LOC, 1)),   # decreasing between sequences 1 and 2
+    ([0, 2, 3, 7], (pc.START_LOC, 2)),   # last start past the 6 query rows
+])
+def test_start_locations(loc, want):
+    assert attn(loc=np.asarray(loc, I32)) == want
+    assert write(loc=np.asarray(loc, I32)) == want
+
+
+def test_query_counts():
+    # sequence 1 has no query: fine for a write, not for attention
+    loc = np.asarray([0, 2, 2, 5], I32)
+    assert attn(loc=loc, T=5) == (pc.QUERY_COUNT, 1)
+    assert write(loc=loc, T=5) is None
+    # three queries in sequence 2 but a bound of 2
+    assert attn(mql=2) == (pc.QUERY_COUNT, 2)
+
+
+@pytest.mark.parametrize("s,L,want_attn,want_write", [
+    (0, 1, (pc.CONTEXT_LEN, 0), (pc.CONTEXT_LEN, 0)),    # fewer tokens (1) than new ones (2)
+    (1, 17, (pc.CONTEXT_LEN, 1), (pc.CONTEXT_LEN, 1)),   # longer than 4 entries x 4 slots
+    (2, 12, None, None),                                  # 12 tokens: entry 2 (block 9) is
+])                                                        # the last one used -> still valid
+def test_context_lengths(s, L, want_attn, want_write):
+    lens = LENS.copy()
+    lens[s] = L
+    assert attn(lens=lens) == want_attn
+    assert write(lens=lens) == want_write
+
+
+def test_context_length_above_host_bound():
+    assert attn(mcl=8) == (pc.CONTEXT_LEN, 2)   # sequence 2 has 9 tokens
+
+
+def test_block_ids():
+    t = TABLES.copy()
+    t[2, 0] = -1        # an entry attention reads but the write (tokens 6..8: entries 1, 2) not
+    assert attn(tables=t) == (pc.BLOCK_ID, 2)
+    assert write(tables=t) is None
+    t = TABLES.copy()
+    t[0, 1] = NB        # the block of sequence 0's new tokens 4, 5
+    assert attn(tables=t) == (pc.BLOCK_ID, 0)
+    assert write(tables=t) == (pc.BLOCK_ID, 0)
+    t = TABLES.copy()
+    t[0, 0] = -1        # sequence 0 writes positions 4, 5: entry 1 only
+    assert attn(tables=t) == (pc.BLOCK_ID, 0)
+    assert write(tables=t) is None
+    t = TABLES.copy()
+    t[1, 3] = 99        # an entry past the used ones: never read
+    assert attn(tables=t) is None and write(tables=t) is None
+
+
+def test_block_ids_with_window():
+    # sequence 2 (9 tokens, queries at 6, 7, 8): a window of 3 reaches back to key 4 (entry 1)
+    t = TABLES.copy()
+    t[2, 0] = -1        # entry 0 (keys 0..3) is outside every query's window
+    assert attn(tables=t, window=3) is None
+    assert attn(tables=t, window=4) == (pc.BLOCK_ID, 2)   # query 6 now sees key 3
+
+
+def test_slot_reused():
+    # sequences 0 and 1 both append into block 7 at slot 1 (positions 5 and 1)
+    t = bt([3, 7], [7], [5, 2, 9], width=4)
+    lens = np.asarray([6, 2, 9], I32)
+    assert write(tables=t, lens=lens) == (pc.SLOT_REUSED, 0)
+    # the same block, different slots: allowed
+    lens = np.asarray([6, 3, 9], I32)
+    assert write(tables=t, lens=lens) is None
+    # two new tokens of one sequence cannot collide; a later sequence that repeats an
+    # earlier one's table does: every writer is reported, the lowest index kept
+    t = bt([3, 7], [0], [3, 7], width=4)
+    lens = np.asarray([6, 4, 6], I32)
+    loc = np.asarray([0, 2, 3, 5], I32)
+    assert write(tables=t, lens=lens, loc=loc, T=5) == (pc.SLOT_REUSED, 0)
+
+
+def test_lowest_kind_then_lowest_index_wins():
+    t = TABLES.copy()
+    t[0, 0] = -3                      # BLOCK_ID at 0
+    lens = LENS.copy()
+    lens[2] = 1                       # CONTEXT_LEN at 2
+    assert attn(tables=t, lens=lens) == (pc.CONTEXT_LEN, 2)
+    t[2, 2] = 50                      # a second BLOCK_ID, at 2
+    assert attn(tables=t) == (pc.BLOCK_ID, 0)
+
+
+@pytest.mark.parametrize("pairs,same,want", [
+    ([(1, 2), (3, 4)], True, None),
+    ([(1, 2), (1, 4)], True, None),                  # one source, two copies
+    ([(1, 2), (-1, 4)], True, (pc.PAIR_ID, 1)),
+    ([(1, 10), (3, 4)], True, (pc.PAIR_ID, 0)),
+    ([(1, 2), (3, 2), (5, 6)], True, (pc.DEST_REUSED, 0)),
+    ([(1, 2), (2, 4)], True, (pc.DEST_IS_SOURCE, 1)),  # block 2 is written and read
+    ([(1, 2), (2, 4)], False, None),                 # two pools: src 2 and dst 2 differ
+    ([(2, 2)], True, (pc.DEST_IS_SOURCE, 0)),
+    ([(9, 2), (3, 9)], False, (pc.PAIR_ID, 1)),      # swap into a 5-block pool
+])
+def test_pairs(pairs, same, want):
+    nd = 10 if same else 5
+    assert pc.check_pairs(np.asarray(pairs, I32).reshape(-1, 2), 10, nd, same) == want
+
+
+def test_block_manager_batches_pass():
+    rng = np.random.default_rng(7)
+    B = 8
+    mgr = BlockManager(400, B)
+    tables = []
+    for _ in range(6):
+        t = []
+        mgr.append_slots(t, int(rng.integers(1, 60)))
+        tables.append(t)
+        for _ in range(int(rng.integers(0, 3))):
+            tables.append(mgr.fork(t))
+    mgr.take_copies()
+    for step in range(5):
+        lens_before = [mgr.num_tokens(t) for t in tables]
+        news = [int(rng.integers(0, 4)) for _ in tables]
+        for t, n in zip(tables, news):
+            mgr.append_slots(t, n)
+        pairs = mgr.take_copies()
+        lens = np.asarray([lb + n for lb, n in zip(lens_before, news)], I32)
+        loc = np.concatenate([[0], np.cumsum(news)]).astype(I32)
+        arr = tables_to_array(tables)
+        assert pc.check_pairs(pairs, 400, 400, True) is None, step
+        assert pc.check_write(arr, lens, loc, 400, B, int(loc[-1])) is None, step
+        # attention: one query per sequence
+        assert pc.check_attention(arr, lens, None, 400, B, len(tables), int(lens.max()),
+                                  1) is None, step
+
+
+def test_skipping_copy_on_write_is_caught():
+    """Two forks appending into their shared last block without the copy: a slot clash."""
+    B = 8
+    mgr = BlockManager(20, B)
+    a = []
+    mgr.append_slots(a, 5)
+    b = mgr.fork(a)
+    arr = tables_to_array([a, b])
+    lens = np.asarray([6, 6], I32)   # both write position 5 into the shared block
+    assert pc.check_write(arr, lens, None, 20, B, 2) == (pc.SLOT_REUSED, 0)
