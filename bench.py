@@ -235,7 +235,13 @@ def bench_config(args) -> int:
     from paged_kv_cache_40_amd import api
     from workloads import CONFIG_NAMES, make_config
 
-    w = make_config(args.config, seed=args.config if args.seed == 5 else args.seed)
+    extra = {"num_heads": args.heads} if args.heads else {}
+    w = make_config(args.config, seed=args.config if args.seed == 5 else args.seed, **extra)
+    workload = CONFIG_NAMES[args.config]
+    if args.heads:  # one GPU's share of a batch whose heads are split over several GPUs
+        full = make_config(args.config, seed=args.config if args.seed == 5 else args.seed)
+        workload += (f"; one GPU's share with the {full.num_heads} heads split "
+                     f"{full.num_heads // args.heads} ways: {args.heads} heads")
     t = w.device_tensors("cuda")
     need = api.pa_decode_workspace_bytes(w.num_queries, w.num_heads, w.head_dim,
                                          w.max_context_len)
@@ -276,7 +282,7 @@ def bench_config(args) -> int:
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": CONFIG_NAMES[args.config], "num_seqs": w.num_seqs,
+        "config": {"workload": workload, "num_seqs": w.num_seqs,
                    "num_heads": w.num_heads, "head_dim": w.head_dim, "block_size": B,
                    "num_blocks": w.num_blocks, "num_queries": w.num_queries,
                    "num_writes": w.num_writes,
@@ -693,7 +699,12 @@ def main(argv=None) -> int:
                     help="never pass the shared-blocks hint (for comparison)")
     ap.add_argument("--prefix", type=int, default=0,
                     help="time shared-prefix prefill, cold vs prefix-cached (own line)")
+    ap.add_argument("--heads", type=int, default=0,
+                    help="with --config 2-5: that batch with this many heads (one GPU's share "
+                         "when the heads are split over several GPUs), own line")
     args = ap.parse_args(argv)
+    if args.heads and args.config == 1:
+        ap.error("--heads applies to --config 2-5 (the tiny batch has fixed shapes)")
 
     if args.gpus != 1:
         print(f"bench.py: the paged-attention path is measured on exactly one GPU; --gpus {args.gpus} is not "
@@ -708,7 +719,7 @@ def main(argv=None) -> int:
 
     _lib.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    if args.config != 5:
+    if args.config != 5 or args.heads:
         return bench_config(args)
     if args.window or args.alibi:
         return bench_variant(args)

@@ -31,6 +31,7 @@ struct DecodeArgs {
   uint32_t flags;          // kDecode* bits
   void* workspace;         // caller's scratch (see decode_workspace_bytes)
   // set by the launcher:
+  int32_t heads_per_wg;    // waves (one head each) per workgroup
   int32_t num_parts_max;   // partition slots per (query row, head) in the workspace
   int32_t part_size;       // tokens per context partition
   float* ws_acc;           // [num_tokens][num_heads][num_parts_max][head_dim]
