@@ -212,7 +212,8 @@ int pa_decode_ext(void* out, const void* q, const void* k_pool, const void* v_po
   ta.scale_log2 = a.scale_log2;
   ta.window = sliding_window;
   ta.alibi = alibi_slopes;
-  return launch_status(pa::launch_tile(ta, head_dim, block_size, max_query_len, st));
+  return launch_status(
+      pa::launch_tile(ta, workspace, head_dim, block_size, max_query_len, max_context_len, st));
 }
 
 size_t pa_check_workspace_bytes(int64_t num_marks) {

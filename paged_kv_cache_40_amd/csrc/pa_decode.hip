@@ -430,7 +430,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
 
 size_t decode_workspace_bytes(int64_t num_tokens, int64_t num_heads, int64_t head_dim,
                               int64_t max_context_len) {
-  const int64_t nparts = (max_context_len + kMinPartition - 1) / kMinPartition;
+  const int64_t nparts = workspace_parts(static_cast<int>(max_context_len));
   if (nparts <= 1) return 0;
   return static_cast<size_t>(num_tokens * num_heads * nparts * (head_dim + 2) * 4);
 }
@@ -447,10 +447,11 @@ static hipError_t launch_decode_t(const DecodeArgs& a0, int max_context_len, hip
   DecodeArgs a = a0;
   a.part_size = P;
   const int nparts = (decode_span(a, BS, max_context_len) + P - 1) / P;
-  a.num_parts_max = nparts;
-  // ws_ml follows ws_acc; both fit the workspace sized for kMinPartition-token partitions
+  // slots at the workspace's common stride (P >= kMinPartition, so nparts fits); ws_ml
+  // follows ws_acc
+  a.num_parts_max = workspace_parts(max_context_len);
   a.ws_acc = static_cast<float*>(a.workspace);
-  a.ws_ml = a.ws_acc + static_cast<int64_t>(a.num_tokens) * a.num_heads * nparts * D;
+  a.ws_ml = a.ws_acc + static_cast<int64_t>(a.num_tokens) * a.num_heads * a.num_parts_max * D;
   a.heads_per_wg = a.num_heads % kHeadsPerWg == 0 ? kHeadsPerWg : 1;
   const int hgroups = a.num_heads / a.heads_per_wg;
   const dim3 block1(kWave * a.heads_per_wg);

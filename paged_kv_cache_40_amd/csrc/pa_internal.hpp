@@ -54,10 +54,26 @@ struct TileArgs {
   float scale_log2;
   int32_t window;          // sliding window in tokens (0 = none)
   const float* alibi;      // per-head ALiBi slopes [num_heads] or nullptr
+  int32_t block_size;
+  // Key splits: a tile whose key steps exceed split_steps is spread over up to splits_max
+  // workgroups (the last takes the rest), each writing fp32 partials to the workspace, merged
+  // by a second pass.  split_steps = 0: one workgroup per tile.
+  int32_t split_steps;
+  int32_t splits_max;
+  int32_t num_parts_max;   // partition slots per (query row, head) in the workspace
+  float* ws_acc;           // [num_tokens][num_heads][num_parts_max][head_dim]
+  float* ws_ml;            // [num_tokens][num_heads][num_parts_max][2] = (max, sum), log2 domain
 };
 
 // Smallest context partition any decode launch uses; sizes the workspace.
 constexpr int kMinPartition = 256;
+
+// Partition slots per (query row, head) in the workspace: one per kMinPartition tokens of the
+// longest context.  Decode partitions and tile key splits both index slots with this stride,
+// so the slots of different query rows never overlap.
+inline int workspace_parts(int max_context_len) {
+  return (max_context_len + kMinPartition - 1) / kMinPartition;
+}
 
 // Workspace bytes for the partial results of a decode launch (0 when no
 // sequence spans more than one partition).
@@ -67,8 +83,9 @@ size_t decode_workspace_bytes(int64_t num_tokens, int64_t num_heads, int64_t hea
 // dtype: 0 = fp32, 1 = fp16.  Return hipSuccess or the launch error.
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int block_size,
                          int max_context_len, hipStream_t stream);
-hipError_t launch_tile(const TileArgs& a, int head_dim, int block_size, int max_query_len,
-                       hipStream_t stream);
+// a.workspace-derived fields (split_steps .. ws_ml) are set by the launcher.
+hipError_t launch_tile(const TileArgs& a, void* workspace, int head_dim, int block_size,
+                       int max_query_len, int max_context_len, hipStream_t stream);
 hipError_t launch_write_kv(void* k_pool, void* v_pool, int64_t num_blocks, const void* k_new,
                            const void* v_new, const int32_t* block_tables, int32_t max_blocks,
                            const int32_t* context_lens, const int32_t* write_start_loc,

@@ -59,6 +59,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "pa_common.hpp"
 #include "pa_internal.hpp"
 
@@ -115,6 +117,28 @@ __device__ __forceinline__ f32x4v mfma16(const f16x8& a, const f16x8& b, const f
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Workgroups a tile of `steps` key steps is split over (the tile and merge kernels agree).
+__device__ __forceinline__ int tile_splits(const TileArgs& a, int steps) {
+  if (a.split_steps <= 0 || steps <= a.split_steps) return 1;
+  const int ns = (steps + a.split_steps - 1) / a.split_steps;
+  return ns < a.splits_max ? ns : a.splits_max;
+}
+
+// Tuning of the key splits: split when a launch has fewer than kSplitTargetWgs tile
+// workgroups, into about kSplitTargetWgs / workgroups splits of at least kMinSplitSteps
+// steps.  512 = one round of the chip (two tile workgroups per CU): measured on the mixed
+// chunk + decode batch at 32/16/8/4 heads, splitting pays only below it (4 heads: 94 vs
+// 134 us, 8 heads: 151 vs 167 us); at 16 heads (512 workgroups) splitting into 2 costs 25%
+// and at 32 heads into 2-4 costs 25-30% (partial writes, merge, re-staged keys).
+#ifndef PA_TILE_SPLIT_TARGET
+#define PA_TILE_SPLIT_TARGET 512
+#endif
+#ifndef PA_TILE_MIN_SPLIT_STEPS
+#define PA_TILE_MIN_SPLIT_STEPS 16
+#endif
+constexpr int64_t kSplitTargetWgs = PA_TILE_SPLIT_TARGET;
+constexpr int kMinSplitSteps = PA_TILE_MIN_SPLIT_STEPS;
+
 }  // namespace
 
 #ifndef PA_TILE_WAVES_PER_EU
@@ -126,7 +150,7 @@ __device__ __forceinline__ f32x4v mfma16(const f16x8& a, const f16x8& b, const f
 #define PA_TILE_OCCUPANCY
 #endif
 
-template <int D, int BS, bool kWindow, bool kAlibi>
+template <int D, int BS, bool kWindow, bool kAlibi, bool kSplit>
 __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(TileArgs a) {
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
   using G = TileGeom<D>;
@@ -138,9 +162,13 @@ __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(T
   lf16* const lds_k = (lf16*)(lds_k_);
   lf16* const lds_v = (lf16*)(lds_v_);
 
-  // head fastest, then query tile (the last tiles, which see the most keys, first), then sequence
+  // head fastest, then (query tile, key split) with the last tiles, which see the most keys,
+  // first, then sequence
   const int h = blockIdx.x;
-  const int tile = static_cast<int>(gridDim.y) - 1 - static_cast<int>(blockIdx.y);
+  const int splits_max = kSplit ? a.splits_max : 1;
+  const int tile = static_cast<int>(gridDim.y) / splits_max - 1 -
+                   static_cast<int>(blockIdx.y) / splits_max;
+  const int split = kSplit ? static_cast<int>(blockIdx.y) % splits_max : 0;
   const int s = blockIdx.z;
   const int t = threadIdx.x;
   const int w = t >> 6;  // wave index
@@ -176,6 +204,12 @@ __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(T
   const int W = kWindow ? a.window : 0;  // compile-time 0 without a window
   const int wg_key_lo = W > 0 ? max(0, ctx - n + q0 - W + 1) : 0;
   const int step_lo = wg_key_lo / kStep;
+  // This workgroup's steps: the whole range, or one split of it (the last split takes the rest).
+  // Without splits (compile time) the range is the tile's own and the loop compiles as such.
+  const int nsplit = kSplit ? tile_splits(a, nsteps - step_lo) : 1;
+  if (split >= nsplit) return;
+  const int first_step = kSplit ? step_lo + split * a.split_steps : step_lo;
+  const int end_step = !kSplit || split == nsplit - 1 ? nsteps : first_step + a.split_steps;
   const int wave_hi_step = wave_last >= 0 ? wave_last / kStep : -1;
   const int wave_lo_step = W > 0 ? max(0, wave_first_pos - W + 1) / kStep : 0;
   // ALiBi: slope_h * (j - p) is added to q.k_j / sqrt(d); in the raw units of the scores here
@@ -383,13 +417,13 @@ __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(T
   // One pipelined step: values of `step` (scores in `cur`), scores of step+1 into `nxt`.
   // LDS buffers are numbered from the first step of the workgroup.
   auto iteration = [&](int step, f32x4v (&cur)[2][2], f32x4v (&nxt)[2][2]) {
-    const int rel = step - step_lo;
+    const int rel = step - first_step;
     const int b_cur = rel % kBufs;
     const int b_nxt = (rel + 1) % kBufs;
-    if (step + 2 < nsteps) stage((rel + 2) % kBufs);
-    if (step + 3 < nsteps) {
+    if (step + 2 < end_step) stage((rel + 2) % kBufs);
+    if (step + 3 < end_step) {
       fetch(step + 3, blk_next);
-      if (step + 4 < nsteps) blk_next = block_of(step + 4);
+      if (step + 4 < end_step) blk_next = block_of(step + 4);
     }
     const int base = step * kStep;
     const bool cur_on = step >= wave_lo_step && step <= wave_hi_step;
@@ -412,58 +446,161 @@ __global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(T
   };
 
   // prologue: the first two steps staged, the third in flight, scores of the first step
-  blk_next = block_of(step_lo);
-  fetch(step_lo, blk_next);
+  blk_next = block_of(first_step);
+  fetch(first_step, blk_next);
   stage(0);
-  if (step_lo + 1 < nsteps) {
-    fetch(step_lo + 1, block_of(step_lo + 1));
+  if (first_step + 1 < end_step) {
+    fetch(first_step + 1, block_of(first_step + 1));
     stage(1);
   }
-  if (step_lo + 2 < nsteps) fetch(step_lo + 2, block_of(step_lo + 2));
-  if (step_lo + 3 < nsteps) blk_next = block_of(step_lo + 3);
+  if (first_step + 2 < end_step) fetch(first_step + 2, block_of(first_step + 2));
+  if (first_step + 3 < end_step) blk_next = block_of(first_step + 3);
   __syncthreads();
   f32x4v sa[2][2], sb[2][2];
-  if (wave_lo_step == step_lo && wave_hi_step >= step_lo) scores(0, step_lo * kStep, sa);
+  if (wave_lo_step <= first_step && first_step <= wave_hi_step)
+    scores(0, first_step * kStep, sa);
 
-  int step = step_lo;
-  for (; step + 1 < nsteps; step += 2) {
+  int step = first_step;
+  for (; step + 1 < end_step; step += 2) {
     iteration(step, sa, sb);
     iteration(step + 1, sb, sa);
   }
-  if (step < nsteps) iteration(step, sa, sb);
+  if (step < end_step) iteration(step, sa, sb);
 
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     // denominator of this lane's query: row 0 of the ones product, held by lane (0, lr)
     const float total = __shfl(den[qt][0], lr, kWave);
     if (q[qt] >= n) continue;
-    const float inv = 1.f / total;
-    f16* op = static_cast<f16*>(a.out) +
-              (static_cast<int64_t>(q_first + q[qt]) * a.num_heads + h) * kD;
+    const int64_t row = static_cast<int64_t>(q_first + q[qt]) * a.num_heads + h;
+    if (!kSplit || nsplit == 1) {
+      const float inv = 1.f / total;
+      f16* op = static_cast<f16*>(a.out) + row * kD;
 #pragma unroll
-    for (int j = 0; j < G::kJ; ++j) {
-      f16x4 o;
+      for (int j = 0; j < G::kJ; ++j) {
+        f16x4 o;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = static_cast<f16>(acc[qt][j][i] * inv);
-      *reinterpret_cast<f16x4*>(op + 16 * j + 4 * lg) = o;
+        for (int i = 0; i < 4; ++i) o[i] = static_cast<f16>(acc[qt][j][i] * inv);
+        *reinterpret_cast<f16x4*>(op + 16 * j + 4 * lg) = o;
+      }
+    } else {
+      // this split's partial: unnormalised O^T rows, (reference m*c, sum) in log2 units;
+      // a query with no key in the split has m = -inf and weight 0 in the merge
+      const int64_t slot = row * a.num_parts_max + split;
+      float* wp = a.ws_acc + slot * kD;
+#pragma unroll
+      for (int j = 0; j < G::kJ; ++j) *reinterpret_cast<f32x4v*>(wp + 16 * j + 4 * lg) = acc[qt][j];
+      if (lg == 0) {
+        a.ws_ml[2 * slot] = m[qt] == -INFINITY ? -INFINITY : mc[qt];
+        a.ws_ml[2 * slot + 1] = total;
+      }
     }
   }
 }
 
-hipError_t launch_tile(const TileArgs& a, int head_dim, int block_size, int max_query_len,
-                       hipStream_t stream) {
+// Merge of split tiles: for each query row and head, M = max_p m_p and
+// o = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p over the tile's splits (the online-
+// softmax merge rule, as for decode partitions).  One workgroup per (head, 8 rows of a tile,
+// sequence), 32 lanes per row: the partial loads of different splits are independent, so a
+// row's latency is about one load, and the many small workgroups keep enough in flight.
+constexpr int kMergeRows = 8;
+constexpr int kMergeGroups = kTileQ / kMergeRows;
+
+template <int D>
+__global__ __launch_bounds__(256) void tile_merge_kernel(TileArgs a) {
+  constexpr int kPer = D / 32;  // dims per lane: 4 or 2
+  const int h = blockIdx.x;
+  const int tile = static_cast<int>(blockIdx.y) / kMergeGroups;
+  const int s = blockIdx.z;
+  const int q_first = a.q_start_loc[s];
+  const int n = a.q_start_loc[s + 1] - q_first;
+  if (n <= 1) return;
+  const int q0 = tile * kTileQ;
+  const int r = q0 + (static_cast<int>(blockIdx.y) % kMergeGroups) * kMergeRows +
+                static_cast<int>(threadIdx.x >> 5);
+  if (r >= n) return;
+  const int ctx = min(a.context_lens[s], a.max_blocks * a.block_size);
+  if (n > ctx || q_first < 0 || q_first + n > a.num_tokens) return;
+  // the tile kernel's step range and split count for this tile
+  const int wg_last = ctx - n + min(q0 + kTileQ - 1, n - 1);
+  const int nsteps = wg_last / kStep + 1;
+  const int wg_key_lo = a.window > 0 ? max(0, ctx - n + q0 - a.window + 1) : 0;
+  const int nsplit = tile_splits(a, nsteps - wg_key_lo / kStep);
+  if (nsplit <= 1) return;
+  const int c = threadIdx.x & 31;
+  const int64_t row = static_cast<int64_t>(q_first + r) * a.num_heads + h;
+  const int64_t slot0 = row * a.num_parts_max;
+  const float* ml = a.ws_ml + slot0 * 2;
+  float M = -INFINITY;
+  for (int p = 0; p < nsplit; ++p) M = fmaxf(M, ml[2 * p]);
+  float L = 0.f;
+  float o[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) o[i] = 0.f;
+  const float* acc = a.ws_acc + slot0 * D + c * kPer;
+#pragma unroll 4
+  for (int p = 0; p < nsplit; ++p) {
+    const float w = fast_exp2(ml[2 * p] - M);
+    L = fmaf(w, ml[2 * p + 1], L);
+    const float* ap = acc + static_cast<int64_t>(p) * D;
+    if constexpr (kPer == 4) {
+      const f32x4v v = *reinterpret_cast<const f32x4v*>(ap);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = fmaf(w, v[i], o[i]);
+    } else {
+      const float2 v = *reinterpret_cast<const float2*>(ap);
+      o[0] = fmaf(w, v.x, o[0]);
+      o[1] = fmaf(w, v.y, o[1]);
+    }
+  }
+  const float inv = 1.f / L;
+  f16* op = static_cast<f16*>(a.out) + row * D + c * kPer;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) op[i] = static_cast<f16>(o[i] * inv);
+}
+
+hipError_t launch_tile(const TileArgs& a0, void* workspace, int head_dim, int block_size,
+                       int max_query_len, int max_context_len, hipStream_t stream) {
   if (head_dim != 64 && head_dim != 128) return hipErrorInvalidValue;
+  TileArgs a = a0;
+  a.block_size = block_size;
   const int tiles = (max_query_len + kTileQ - 1) / kTileQ;
-  dim3 grid(a.num_heads, tiles, a.num_seqs);
+  // Key splits, when the launch has too few tile workgroups to fill the chip: the chunks hold
+  // at least ceil((num_tokens - num_seqs) / kTileQ) tiles (every sequence has one query row
+  // outside the count).  Partials use the workspace at its common slot stride.
+  a.num_parts_max = workspace_parts(max_context_len);
+  a.ws_acc = static_cast<float*>(workspace);
+  a.ws_ml = a.ws_acc + static_cast<int64_t>(a.num_tokens) * a.num_heads * a.num_parts_max *
+                           head_dim;
+  a.split_steps = 0;
+  a.splits_max = 1;
+  const int max_steps = (max_context_len + kStep - 1) / kStep;
+  const int64_t wgs =
+      std::max<int64_t>(1, (int64_t{a.num_tokens} - a.num_seqs + kTileQ - 1) / kTileQ) *
+      a.num_heads;
+  if (workspace != nullptr && a.num_parts_max > 1 && wgs < kSplitTargetWgs) {
+    const int want = static_cast<int>((kSplitTargetWgs + wgs - 1) / wgs);
+    const int ss = std::max((max_steps + want - 1) / want, kMinSplitSteps);
+    const int ns = std::min((max_steps + ss - 1) / ss, a.num_parts_max);
+    if (ss < max_steps && ns > 1 && int64_t{tiles} * std::max(ns, kMergeGroups) <= 65535) {
+      a.split_steps = ss;
+      a.splits_max = ns;
+    }
+  }
+  dim3 grid(a.num_heads, tiles * a.splits_max, a.num_seqs);
   const bool window = a.window > 0;
   const bool alibi = a.alibi != nullptr;
+  const bool split = a.splits_max > 1;
   auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a); };
   // (head_dim, block size, window, ALiBi) pick one instantiation
+#define PA_TILE_SPLITS(D_, B_, W_, A_)                                             \
+  if (split) go(tile_attention_kernel<D_, B_, W_, A_, true>);                      \
+  else go(tile_attention_kernel<D_, B_, W_, A_, false>);
 #define PA_TILE_VARIANTS(D_, B_)                                                   \
-  if (window && alibi) go(tile_attention_kernel<D_, B_, true, true>);              \
-  else if (window) go(tile_attention_kernel<D_, B_, true, false>);                 \
-  else if (alibi) go(tile_attention_kernel<D_, B_, false, true>);                  \
-  else go(tile_attention_kernel<D_, B_, false, false>);
+  if (window && alibi) { PA_TILE_SPLITS(D_, B_, true, true) }                      \
+  else if (window) { PA_TILE_SPLITS(D_, B_, true, false) }                         \
+  else if (alibi) { PA_TILE_SPLITS(D_, B_, false, true) }                          \
+  else { PA_TILE_SPLITS(D_, B_, false, false) }
 #define PA_TILE_BLOCKS(D_)                                                         \
   switch (block_size) {                                                            \
     case 8: PA_TILE_VARIANTS(D_, 8) break;                                         \
@@ -478,6 +615,14 @@ hipError_t launch_tile(const TileArgs& a, int head_dim, int block_size, int max_
   }
 #undef PA_TILE_BLOCKS
 #undef PA_TILE_VARIANTS
+#undef PA_TILE_SPLITS
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || a.splits_max <= 1) return err;
+  dim3 grid2(a.num_heads, tiles * kMergeGroups, a.num_seqs);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(tile_merge_kernel<128>, grid2, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(tile_merge_kernel<64>, grid2, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -369,6 +369,18 @@ def test_chunk_tiles_head_dim_64(B):
     full_check(w)
 
 
+@pytest.mark.parametrize("head_dim,B", [(128, 16), (64, 8), (128, 32)])
+def test_chunk_key_splits(head_dim, B):
+    """Few tile workgroups (2 heads, a handful of chunks), so the launch splits long tiles'
+    keys over several workgroups and merges their partials: priors from 0 to 9,000 keys (one
+    to ~18 splits, the last split shorter or a single step), chunks of 2..300 queries whose
+    diagonal falls inside or across splits, next to decodes."""
+    chunks = [(0, 2), (511, 2), (600, 40), (3000, 128), (9000, 129), (1537, 300)]
+    w = make_custom_mixed(60 + B + head_dim, 2, B, chunks, [1, 2500, 9001],
+                          name=f"chunk_splits_d{head_dim}_B{B}", head_dim=head_dim)
+    full_check(w)
+
+
 def test_chunk_tiles_peaked_scores():
     w = make_custom_mixed(41, 3, 16, [(200, 100), (0, 70)], [50], name="chunks_peaked",
                           q_scale=4.0)

@@ -178,6 +178,17 @@ def test_chunk_window_alibi_head_dim_64(window, use_alibi):
     variant_check(w, window, geometric_slopes(3) if use_alibi else None)
 
 
+@pytest.mark.parametrize("window,use_alibi", [(700, False), (700, True), (2000, True),
+                                              (0, True)])
+def test_chunk_window_alibi_key_splits(window, use_alibi):
+    """Long priors with 2 heads, so tiles are split over several workgroups: splits that
+    start at the window's first step, windows spanning two to four splits, and ALiBi biases
+    carried through the partial merge."""
+    chunks = [(3000, 129), (6000, 40), (900, 300), (0, 70)]
+    w = make_custom_mixed(79, 2, 16, chunks, [1, 4000], name=f"chunk_splits_W{window}")
+    variant_check(w, window, geometric_slopes(2) if use_alibi else None)
+
+
 def test_chunk_history_before_window_is_never_used():
     """Chunks whose keys older than the first query's window hold NaN, with the table entries
     of blocks wholly before it set to -1 (poisoned before any library call; this step's rows,
