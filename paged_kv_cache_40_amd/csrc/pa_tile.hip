@@ -56,6 +56,12 @@
 // this file).  Values of keys at or past the context length are zeroed when
 // staged (those pool slots may hold anything); keys past a query's position
 // are masked.  Waves whose queries all lie past the chunk's end only stage.
+//
+// Key splits (a compile-time variant): a launch with too few tiles to fill the
+// chip gives each tile's key steps to several workgroups, each of which writes
+// per-query partials (unnormalised output rows, max and sum) to the workspace;
+// tile_merge_kernel combines them with the same online-softmax rule the decode
+// merge uses [P2 "PagedAttentionの仕組み", online softmax remark].
 
 #include <math.h>
 
