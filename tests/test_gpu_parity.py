@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from paged_kv_cache_40_amd import api
 from workloads import make_config, make_small, make_custom_decode, make_custom_mixed
 from paged_harness import (assert_bits_equal, assert_close, host_copy, log, oracle_step,
@@ -182,6 +183,87 @@ def test_block_permutation_bit_identical():
         outs.append(_decode(q, kp, vp, tab, lens))
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+
+
+def test_decode_token_permutation_invariant():
+    """Decode attention is a sum over the context's tokens, so permuting a sequence's
+    (k, v) rows jointly leaves it unchanged up to rounding: the GPU output of every
+    permuted context stays within the fp16 tolerance of the unpermuted one, and both
+    equal the oracle over their own token order.  Unlike a block permutation this
+    changes the order of the kernel's sums (partitions, lanes, merges)."""
+    log("[case] token permutation")
+    lens, B, H, D = [2, 33, 257, 1500, 4100], 16, 4, 128
+    kh, vh, q = _histories(lens, H, D, seed=23)
+    NB = sum(-(-L // B) for L in lens) + 20
+    tab = _tables(np.random.default_rng(3), lens, B, NB)
+    qd = q.cuda()
+    base = _decode(qd, *_pool_from_histories(kh, vh, tab, NB, B, torch.float16), tab, lens)
+    for s, L in enumerate(lens):
+        ref = oracle.attend(q[s:s + 1].numpy(), kh[s].numpy(), vh[s].numpy(), [L - 1])
+        assert_close(base[s:s + 1].cpu().numpy(), ref, "f16", f"seq {s} unpermuted vs oracle")
+    rng = np.random.default_rng(4)
+    for trial in range(2):
+        perms = [torch.from_numpy(rng.permutation(L)) for L in lens]
+        khp = [k[p] for k, p in zip(kh, perms)]
+        vhp = [v[p] for v, p in zip(vh, perms)]
+        out = _decode(qd, *_pool_from_histories(khp, vhp, tab, NB, B, torch.float16), tab, lens)
+        # each run is within the fp16 tolerance of the exact value, so within twice of each other
+        o, b = out.cpu().numpy().astype(np.float64), base.cpu().numpy().astype(np.float64)
+        assert (np.abs(o - b) <= 2 * (2e-3 + 1e-2 * np.abs(b))).all(), f"trial {trial}"
+        for s, L in enumerate(lens):
+            ref = oracle.attend(q[s:s + 1].numpy(), khp[s].numpy(), vhp[s].numpy(), [L - 1])
+            assert_close(out[s:s + 1].cpu().numpy(), ref, "f16", f"seq {s} vs oracle")
+    log("[ok]")
+
+
+def _chunk_call(q, kp, vp, tables, lens, qlens):
+    """pa_decode over sequences with qlens[s] query rows each (chunks and decodes)."""
+    bt = torch.tensor(tables, dtype=torch.int32).cuda()
+    cl = torch.tensor(lens, dtype=torch.int32).cuda()
+    loc = torch.tensor(np.concatenate([[0], np.cumsum(qlens)]), dtype=torch.int32).cuda()
+    out = torch.empty_like(q)
+    api.pa_decode(out, q, kp, vp, bt, cl, loc, max_context_len=max(lens),
+                  max_query_len=max(qlens))
+    torch.cuda.synchronize()
+    return out
+
+
+def test_closed_forms():
+    """Results fixed by the attention formula alone, checked without the oracle: with every
+    key of a sequence equal, the weights are uniform, so a decode returns the mean of its
+    context's values and chunk query i the mean of values 0..p_i (prefix means); with every
+    value equal to c the output is c.  Decodes of 1 to 5,000 tokens (up to three merged
+    partitions) and chunks over 0 and 700 prior tokens, split into several workgroups."""
+    log("[case] closed forms")
+    B, H, D = 16, 2, 128
+    g = torch.Generator().manual_seed(31)
+    lens = [1, 100, 2049, 5000, 302, 1000]
+    qlens = [1, 1, 1, 1, 300, 300]          # two chunks: priors 2 and 700
+    NB = sum(-(-L // B) for L in lens) + 10
+    tab = _tables(np.random.default_rng(5), lens, B, NB)
+    krow = torch.randn(1, H, D, generator=g).half()
+    kh = [krow.expand(L, H, D).clone() for L in lens]
+    vh = [torch.randn(L, H, D, generator=g).half() for L in lens]
+    q = torch.randn(sum(qlens), H, D, generator=g).half()
+    out = _chunk_call(q.cuda(), *_pool_from_histories(kh, vh, tab, NB, B, torch.float16), tab,
+                      lens, qlens).cpu().numpy().astype(np.float64)
+    row = 0
+    for s, (L, n) in enumerate(zip(lens, qlens)):
+        v = vh[s].numpy().astype(np.float64)
+        prefix_mean = np.cumsum(v, axis=0) / np.arange(1, L + 1)[:, None, None]
+        want = prefix_mean[L - n:L]           # query i at position L-n+i
+        got = out[row:row + n]
+        assert np.abs(got - want).max() <= 2e-3 + 1e-2 * np.abs(want).max(), f"seq {s}"
+        row += n
+    # every value row equal to c: output c (for any keys)
+    c = torch.randn(1, H, D, generator=g).half()
+    kh = [torch.randn(L, H, D, generator=g).half() for L in lens]
+    vh = [c.expand(L, H, D).clone() for L in lens]
+    out = _chunk_call(q.cuda(), *_pool_from_histories(kh, vh, tab, NB, B, torch.float16), tab,
+                      lens, qlens).cpu().numpy().astype(np.float64)
+    want = np.broadcast_to(c.numpy().astype(np.float64), out.shape)
+    assert np.abs(out - want).max() <= 2e-3 + 1e-2 * np.abs(want).max()
+    log("[ok]")
 
 
 def test_shared_prefix_bit_identical():
