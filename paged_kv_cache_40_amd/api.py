@@ -9,6 +9,9 @@ Debug mode (environment variable PA_DEBUG=1 at import, or set_debug(True)):
 every call first runs the library's device-side precondition check for its
 arguments (pa_check_attention / pa_check_write / pa_check_pairs), waits for it,
 and raises PreconditionError instead of launching when a precondition fails.
+The wait synchronizes the stream, so debug mode cannot run under HIP graph
+capture (the C entry points pa_check_* only enqueue; the wrappers here wait
+for the word).
 """
 
 from __future__ import annotations
