@@ -247,7 +247,13 @@ def bench_config(args) -> int:
                                          w.max_context_len)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(t["q"])
-    shared = w.shares_blocks() and not args.no_shared_hint
+    # runs of neighbouring sequences that share blocks: the samples of one prompt
+    group = args.group
+    if group is None:
+        runs = int(w.extra.get("samples", 0))
+        group = runs if 2 <= runs <= 6 and w.dtype == "f16" and not (
+            args.window or args.alibi or args.no_shared_hint) else 0
+    shared = w.shares_blocks() and not args.no_shared_hint and not group
     slopes = None
     if args.alibi:  # the ALiBi paper's geometric slopes
         slopes = torch.tensor(2.0 ** (-8.0 * (np.arange(w.num_heads) + 1) / w.num_heads),
@@ -262,7 +268,7 @@ def bench_config(args) -> int:
         api.pa_decode_ext(out, t["q"], t["k_pool"], t["v_pool"], t["block_tables"],
                           t["context_lens"], t["q_start_loc"], max_context_len=w.max_context_len,
                           max_query_len=w.max_query_len, workspace=ws, shared_blocks=shared,
-                          sliding_window=args.window, alibi_slopes=slopes)
+                          sliding_window=args.window, alibi_slopes=slopes, group=group)
 
     wall_ms, ev_ms = _timed(step, args.steps, args.warmup)
     # the same step after a 1 GiB buffer (4x the 256 MB last-level cache) is rewritten
@@ -287,7 +293,7 @@ def bench_config(args) -> int:
                    "num_blocks": w.num_blocks, "num_queries": w.num_queries,
                    "num_writes": w.num_writes,
                    "copy_pairs": 0 if w.copy_pairs is None else len(w.copy_pairs),
-                   "shared_blocks_hint": shared, "sliding_window": args.window,
+                   "shared_blocks_hint": shared, "group": group, "sliding_window": args.window,
                    "alibi": bool(args.alibi),
                    "kv_bytes_logical": kv, "kv_bytes_unique_blocks": unique},
         "event_ms_per_step": round(ev_ms, 4),
@@ -441,6 +447,10 @@ def bench_beam(args) -> int:
     from workloads.beam import beam_rows_torch, make_beam_tree
 
     W, H, D, B, R, steps = args.beam, 40, 128, 16, 64, args.beam_steps
+    # a request's beams sit next to each other: runs of W for the grouped decode (2..6)
+    group = args.group
+    if group is None:
+        group = W if 2 <= W <= 6 and not args.no_shared_hint else 0
     rng = np.random.default_rng(args.seed)
     prompts = rng.integers(1024, 4097, size=R)
     trees = [make_beam_tree(1000 + i, W, steps, int(P)) for i, P in enumerate(prompts)]
@@ -494,7 +504,8 @@ def bench_beam(args) -> int:
             api.pa_copy_blocks(kp, vp, d["pairs"])
         api.pa_write_kv(kp, vp, d["kn"], d["vn"], d["bt"], d["cl"])
         api.pa_decode_ext(out, d["q"], kp, vp, d["bt"], d["cl"], max_context_len=d["mcl"],
-                          workspace=ws, shared_blocks=not args.no_shared_hint)
+                          workspace=ws, shared_blocks=not (args.no_shared_hint or group),
+                          group=group)
 
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
@@ -516,7 +527,8 @@ def bench_beam(args) -> int:
         "config": {"workload": f"beam search, 64 requests x width {W}, prompts U{{1024..4096}}, "
                                "40 heads, d=128, B=16, fp16, synthetic beam trees",
                    "width": W, "requests": R, "num_blocks": NB,
-                   "shared_blocks_hint": not args.no_shared_hint},
+                   "shared_blocks_hint": not (args.no_shared_hint or group),
+                   "group": group},
         "wall_ms_per_step": round(wall_ms, 4),
         "candidate_tokens_per_s": round(R * W / (ev_ms * 1e-3), 1),
         "unique_block_GBs": round(unique / steps / (ev_ms * 1e-3) / 1e9, 2),
@@ -695,6 +707,10 @@ def main(argv=None) -> int:
     ap.add_argument("--beam", type=int, default=0,
                     help="time beam-search decoding with this beam width instead (own line)")
     ap.add_argument("--beam-steps", type=int, default=64)
+    ap.add_argument("--group", type=int, default=None,
+                    help="grouped decode over runs of this many neighbouring sequences instead "
+                         "of the shared-blocks hint; default: the batch's own runs (the samples "
+                         "of one prompt, the beams of one request); 0: off")
     ap.add_argument("--no-shared-hint", action="store_true",
                     help="never pass the shared-blocks hint (for comparison)")
     ap.add_argument("--prefix", type=int, default=0,

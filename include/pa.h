@@ -78,7 +78,9 @@ typedef enum {
 typedef enum { PA_SWAP_OUT = 0, PA_SWAP_IN = 1 } pa_swap_direction;
 
 /* pa_decode_ext flags */
-typedef enum { PA_DECODE_SHARED_BLOCKS = 1 } pa_decode_flags;
+typedef enum { PA_DECODE_SHARED_BLOCKS = 1, PA_DECODE_GROUP_SHIFT = 8 } pa_decode_flags;
+/* group size g (2..6) for the grouped decode, in flag bits 8..11 */
+#define PA_DECODE_GROUP(g) ((uint32_t)(g) << PA_DECODE_GROUP_SHIFT)
 
 /*
  * pa_write_kv — store this step's new K/V rows into their cache slots.
@@ -166,6 +168,18 @@ int pa_decode(void* out, const void* q,
  *   speed differs.  Unknown bits return PA_ERR_UNSUPPORTED; with the flag,
  *   num_heads * num_seqs * ceil(max_context_len / 256) must stay below 2^24
  *   (PA_ERR_SHAPE).
+ *   PA_DECODE_GROUP(g), g = 2..6, instead: sequences come in runs of g
+ *   (sequences 0..g-1, g..2g-1, ..., the last run possibly shorter) whose
+ *   members may share their leading blocks, as the samples of one prompt or
+ *   the beams of one search do.  Where every member of a run holds the same
+ *   physical blocks at the same positions, those K/V rows are read once for
+ *   the whole run (P1 sec. 6).  The result is the same attention whatever the
+ *   tables hold (the runs only say where to look for sharing); the context
+ *   partitions differ from the plain kernel's, so outputs agree with it within
+ *   rounding, not bit for bit.  Built for dtype PA_F16 with q_start_loc NULL,
+ *   sliding_window 0 and alibi_slopes NULL, and not combined with
+ *   PA_DECODE_SHARED_BLOCKS: other uses return PA_ERR_UNSUPPORTED.  g = 0 or 1
+ *   means no runs.
  * pa_decode(...) is pa_decode_ext(..., 0, NULL, 0, stream).  Both variants
  * apply to every query row, single-query decodes and multi-query chunks alike
  * (a chunk's query at position p sees its own window p-W+1 .. p).

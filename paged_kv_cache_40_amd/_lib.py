@@ -15,6 +15,7 @@ PA_F32, PA_F16 = 0, 1
 PA_OK = 0
 PA_SWAP_OUT, PA_SWAP_IN = 0, 1
 PA_DECODE_SHARED_BLOCKS = 1
+PA_DECODE_GROUP_SHIFT = 8  # group size g of the grouped decode in flag bits 8..11
 PA_CHECK_OK = 0xFFFFFFFFFFFFFFFF
 # pa_check_kind values
 CHECK_KINDS = {1: "START_LOC", 2: "QUERY_COUNT", 3: "CONTEXT_LEN", 4: "BLOCK_ID",

@@ -244,10 +244,13 @@ def pa_decode_ext(out, q, k_pool, v_pool, block_tables, context_lens, q_start_lo
                   max_context_len: Optional[int] = None, max_query_len: int = 1,
                   workspace: Optional[torch.Tensor] = None, sliding_window: int = 0,
                   alibi_slopes: Optional[torch.Tensor] = None, shared_blocks: bool = False,
-                  stream=None) -> torch.Tensor:
+                  stream=None, group: int = 0) -> torch.Tensor:
     """pa_decode with a sliding window (0 = none), optional per-head ALiBi slopes (float32
     GPU tensor [num_heads]) and the shared-blocks scheduling hint (same results, faster when
-    neighbouring sequences share blocks)."""
+    neighbouring sequences share blocks).  group = g in 2..6: sequences come in runs of g
+    whose members may share leading blocks (samples of one prompt, beams of one search); rows
+    every member of a run holds in the same blocks are read once for the run (fp16, one query
+    per sequence, no window or ALiBi, not with shared_blocks)."""
     nb, bs, h, d, dt = _check_pool(k_pool, v_pool)
     S = context_lens.shape[0]
     T = q.shape[0]
@@ -257,6 +260,7 @@ def pa_decode_ext(out, q, k_pool, v_pool, block_tables, context_lens, q_start_lo
     _require(q.shape == (T, h, d) and out.shape == q.shape, "q / out must be [T][H][d]")
     _require(q.dtype == out.dtype == k_pool.dtype, "q / out dtype must match the pool")
     _require(q.is_contiguous() and out.is_contiguous(), "q / out must be contiguous")
+    _require(0 <= int(group) <= 15, "group must be in 0..15 (2..6 are built)")
     if max_context_len is None:
         max_context_len = int(context_lens.max().item())
     need = pa_decode_workspace_bytes(T, h, d, max_context_len)
@@ -275,7 +279,9 @@ def pa_decode_ext(out, q, k_pool, v_pool, block_tables, context_lens, q_start_lo
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), nb, _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), _ptr(q_start_loc), S, T, int(max_context_len),
         int(max_query_len), h, d, bs, dt, _ptr(workspace), ws_bytes, int(sliding_window),
-        _ptr(alibi_slopes), _lib.PA_DECODE_SHARED_BLOCKS if shared_blocks else 0,
+        _ptr(alibi_slopes),
+        (_lib.PA_DECODE_SHARED_BLOCKS if shared_blocks else 0) |
+        (int(group) << _lib.PA_DECODE_GROUP_SHIFT),
         _stream(stream))
     _lib.check(st, "pa_decode")
     return out

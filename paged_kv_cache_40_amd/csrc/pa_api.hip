@@ -147,7 +147,14 @@ int pa_decode_ext(void* out, const void* q, const void* k_pool, const void* v_po
                   const float* alibi_slopes, uint32_t flags, void* stream) {
   if (int st = check_layout(num_blocks, num_heads, head_dim, block_size, dtype)) return st;
   if (sliding_window < 0) return PA_ERR_SHAPE;
-  if (flags & ~static_cast<uint32_t>(PA_DECODE_SHARED_BLOCKS)) return PA_ERR_UNSUPPORTED;
+  const uint32_t group_bits = 0xFu << PA_DECODE_GROUP_SHIFT;
+  if (flags & ~(static_cast<uint32_t>(PA_DECODE_SHARED_BLOCKS) | group_bits))
+    return PA_ERR_UNSUPPORTED;
+  const int group = static_cast<int>((flags & group_bits) >> PA_DECODE_GROUP_SHIFT);
+  if (group > 1 && (group > pa::kMaxDecodeGroup || (flags & PA_DECODE_SHARED_BLOCKS) ||
+                    dtype != PA_F16 || q_start_loc != nullptr || sliding_window != 0 ||
+                    alibi_slopes != nullptr))
+    return PA_ERR_UNSUPPORTED;
   if (num_seqs <= 0 || num_tokens <= 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
   if (max_context_len <= 0 || max_query_len <= 0 || max_query_len > max_context_len)
     return PA_ERR_SHAPE;
@@ -189,7 +196,8 @@ int pa_decode_ext(void* out, const void* q, const void* k_pool, const void* v_po
   a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(head_dim)));
   a.window = sliding_window;
   a.alibi = alibi_slopes;
-  a.flags = flags;
+  a.flags = flags & PA_DECODE_SHARED_BLOCKS;
+  a.group = group > 1 ? group : 0;
   a.workspace = workspace;
   hipStream_t st = static_cast<hipStream_t>(stream);
   // single-query sequences: context partitions + merge; the kernels skip the others

@@ -430,6 +430,311 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   for (int i = 0; i < kPer; ++i) op[i] = static_cast<T>(o[i] * inv);
 }
 
+// Grouped decode [P1 sec. 6: the samples of one prompt and the beams of one search share
+// their leading blocks; P2 "並列サンプリングとビームサーチ"].  When the caller places such
+// sequences next to each other, in runs of G, the shared rows need only be read once for
+// the whole run.  Partitions are fixed (tokens [p*P, (p+1)*P)), so the members' partitions
+// line up.  For each (run, partition) every wave of the run works out, from the members'
+// context lengths and table entries alone:
+//   t = the longest prefix of the partition, in whole trips, that every member's context
+//       covers and whose blocks are the same physical blocks for every member;
+// and the run is handled jointly when t > 0 and no member has more than kRest further
+// tokens in the partition.  Then the run's first wave reads the t tokens' K/V rows once,
+// updates every member's running (m, l, acc) from them, and afterwards takes each member's
+// remaining tokens on its own; the other members' waves exit.  Otherwise each wave reads
+// its own sequence's partition, as the plain kernel does.  Since all waves decide alike,
+// every (sequence, head, partition) is computed exactly once whatever the tables hold: the
+// grouping only says where sharing is likely.  Partials use the plain kernel's workspace
+// slots and merge pass.
+template <int D, int BS, int P, int kCap>
+__global__ __launch_bounds__(64 * kHeadsPerWg) PA_DECODE_OCCUPANCY
+void decode_group_kernel(DecodeArgs a) {
+  using T = f16;
+  using C = DecodeCfg<T, D, BS, P>;
+  constexpr int kRest = P / 8;  // most tokens past the shared prefix one member may add
+  const int hg = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
+  const int h = hg * a.heads_per_wg + static_cast<int>(threadIdx.x >> 6);
+  if (h >= a.num_heads) return;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 3;  // token within a group of 8
+  const int c = lane & 7;   // 16-byte column within a 128-byte line
+
+  const int cap = min(a.max_blocks * BS, a.max_context_len);
+  const int start = part * P;
+  if (min(a.context_lens[s], cap) <= start) return;  // no tokens of this sequence here
+  const int lead = s - s % a.group;
+  const int nmem = min(a.group, a.num_seqs - lead);
+
+  // members' clamped context lengths and their table entries for this partition
+  int ctxk[kCap];
+  int blk[kCap][C::kTabRegs];
+  bool all_in = nmem > 1;
+  int min_ctx = cap, max_ctx = 0;
+#pragma unroll
+  for (int k = 0; k < kCap; ++k) {
+    ctxk[k] = 0;
+#pragma unroll
+    for (int r = 0; r < C::kTabRegs; ++r) blk[k][r] = 0;
+    if (k < nmem) {
+      ctxk[k] = min(a.context_lens[lead + k], cap);
+      all_in = all_in && ctxk[k] > start;
+      min_ctx = min(min_ctx, ctxk[k]);
+      max_ctx = max(max_ctx, ctxk[k]);
+      if (ctxk[k] > start) {
+        const int nb = (min(ctxk[k] - start, P) + BS - 1) / BS;
+        const int32_t* bt =
+            a.block_tables + static_cast<int64_t>(lead + k) * a.max_blocks + start / BS;
+#pragma unroll
+        for (int r = 0; r < C::kTabRegs; ++r) {
+          if (r * kWave + lane < nb) {
+            const int b = bt[r * kWave + lane];
+            blk[k][r] = (b >= 0 && b < a.num_blocks) ? b : 0;
+          }
+        }
+      }
+    }
+  }
+
+  int t = 0;  // shared prefix of the partition, in tokens (a multiple of the trip)
+  if (all_in) {
+    const int reach = min(min_ctx - start, P);  // tokens every member has in the partition
+    const int nchk = (reach + BS - 1) / BS;     // blocks holding them
+    int first_diff = nchk;
+#pragma unroll
+    for (int r = C::kTabRegs - 1; r >= 0; --r) {
+      bool same = true;
+#pragma unroll
+      for (int k = 1; k < kCap; ++k)
+        if (k < nmem) same = same && blk[k][r] == blk[0][r];
+      const uint64_t diff = __ballot(r * kWave + lane < nchk && !same);
+      if (diff != 0) first_diff = r * kWave + __builtin_ctzll(diff);
+    }
+    t = min(first_diff * BS, reach) / C::kTrip * C::kTrip;
+    if (min(max_ctx - start, P) - t > kRest) t = 0;
+  }
+  const bool joint = t > 0;
+  if (joint && s != lead) return;  // the run's first wave computes this partition for all
+  const int base_seq = joint ? lead : s;  // sequence of state slot 0
+  const int nact = joint ? nmem : 1;      // state slots in use
+
+  const int64_t row_stride = static_cast<int64_t>(a.num_heads) * D;
+  auto col = [&](int j) { return (j * 8 + c) * C::kEpc; };
+  const T* kbase = static_cast<const T*>(a.k_pool) + static_cast<int64_t>(h) * D;
+  const T* vbase = static_cast<const T*>(a.v_pool) + static_cast<int64_t>(h) * D;
+
+  u32x4 qc[kCap][C::kCpt];
+  float m[kCap], l[kCap], acc[kCap][C::kEpl];
+#pragma unroll
+  for (int k = 0; k < kCap; ++k) {
+    m[k] = -INFINITY;
+    l[k] = 0.f;
+#pragma unroll
+    for (int e = 0; e < C::kEpl; ++e) acc[k][e] = 0.f;
+#pragma unroll
+    for (int j = 0; j < C::kCpt; ++j) qc[k][j] = u32x4{0, 0, 0, 0};
+    if (k < nact) {
+      const T* qp = static_cast<const T*>(a.q) +
+                    (static_cast<int64_t>(base_seq + k) * a.num_heads + h) * D;
+#pragma unroll
+      for (int j = 0; j < C::kCpt; ++j) qc[k][j] = ld16(qp + col(j));
+    }
+  }
+
+  // row offset of token (group_base + g) through the table entries b (group_base: a
+  // multiple of 8 relative to the partition start, wave-uniform)
+  auto row_offset = [&](const int (&b)[C::kTabRegs], int group_base) -> int64_t {
+    const int bi = group_base / BS;
+    int id;
+    if constexpr (C::kTabRegs == 1) {
+      id = __builtin_amdgcn_readlane(b[0], bi);
+    } else {
+      id = bi < kWave ? __builtin_amdgcn_readlane(b[0], bi)
+                      : __builtin_amdgcn_readlane(b[C::kTabRegs - 1], bi - kWave);
+    }
+    return (static_cast<int64_t>(id) * BS + (group_base % BS) + g) * row_stride;
+  };
+  auto score = [&](const u32x4 (&qv)[C::kCpt], const u32x4 (&kr)[C::kCpt]) {
+    float d = 0.f;
+#pragma unroll
+    for (int j = 0; j < C::kCpt; ++j) d = chunk_dot<T>(qv[j], kr[j], d);
+    return group_sum<8>(d) * a.scale_log2;
+  };
+  auto update = [&](float& mk, float& lk, float (&ak)[C::kEpl], const float (&sc)[C::kG],
+                    const u32x4 (&vr)[C::kG][C::kCpt], const bool (&ok)[C::kG]) {
+    float mx = sc[0];
+#pragma unroll
+    for (int i = 1; i < C::kG; ++i) mx = fmaxf(mx, sc[i]);
+    if (__any(mx > mk + kTau)) {
+      const float mn = fmaxf(mk, mx);
+      const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(mk - mn);
+      lk *= alpha;
+#pragma unroll
+      for (int e = 0; e < C::kEpl; ++e) ak[e] *= alpha;
+      mk = mn;
+    }
+#pragma unroll
+    for (int i = 0; i < C::kG; ++i) {
+      const float p = ok[i] ? fast_exp2(sc[i] - mk) : 0.f;
+      lk += p;
+#pragma unroll
+      for (int j = 0; j < C::kCpt; ++j)
+#pragma unroll
+        for (int e = 0; e < C::kEpc; ++e)
+          ak[j * C::kEpc + e] = fmaf(p, chunk_elt<T>(vr[i][j], e), ak[j * C::kEpc + e]);
+    }
+  };
+
+  // shared prefix: each row read once, every member updated from it
+  if (joint) {
+    bool all_ok[C::kG];
+#pragma unroll
+    for (int i = 0; i < C::kG; ++i) all_ok[i] = true;
+    for (int rel = 0; rel < t; rel += C::kTrip) {
+      u32x4 kr[C::kG][C::kCpt], vr[C::kG][C::kCpt];
+      int64_t off[C::kG];
+#pragma unroll
+      for (int i = 0; i < C::kG; ++i) {
+        off[i] = row_offset(blk[0], rel + i * 8);
+#pragma unroll
+        for (int j = 0; j < C::kCpt; ++j) kr[i][j] = ld_kv<false>(kbase + off[i] + col(j));
+      }
+#pragma unroll
+      for (int i = 0; i < C::kG; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kCpt; ++j) vr[i][j] = ld_kv<false>(vbase + off[i] + col(j));
+#pragma unroll
+      for (int k = 0; k < kCap; ++k) {
+        if (k < nact) {
+          float sc[C::kG];
+#pragma unroll
+          for (int i = 0; i < C::kG; ++i) sc[i] = score(qc[k], kr[i]);
+          update(m[k], l[k], acc[k], sc, vr, all_ok);
+        }
+      }
+    }
+  }
+
+  // one member's own tokens [rel0, end) of the partition (table entries wb), then its result
+  auto finish = [&](const u32x4 (&wq)[C::kCpt], float& wm, float& wl, float (&wacc)[C::kEpl],
+                    const int (&wb)[C::kTabRegs], int rel0, int end, bool single, int seq) {
+    int rel = rel0;
+    for (; rel + C::kTrip <= end; rel += C::kTrip) {
+      u32x4 kr[C::kG][C::kCpt], vr[C::kG][C::kCpt];
+      int64_t off[C::kG];
+      bool ok[C::kG];
+#pragma unroll
+      for (int i = 0; i < C::kG; ++i) {
+        ok[i] = true;
+        off[i] = row_offset(wb, rel + i * 8);
+#pragma unroll
+        for (int j = 0; j < C::kCpt; ++j) kr[i][j] = ld_kv<false>(kbase + off[i] + col(j));
+      }
+#pragma unroll
+      for (int i = 0; i < C::kG; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kCpt; ++j) vr[i][j] = ld_kv<false>(vbase + off[i] + col(j));
+      float sc[C::kG];
+#pragma unroll
+      for (int i = 0; i < C::kG; ++i) sc[i] = score(wq, kr[i]);
+      update(wm, wl, wacc, sc, vr, ok);
+    }
+    if (rel < end) {  // ragged last trip: lanes past the end load nothing
+      u32x4 kr[C::kG][C::kCpt], vr[C::kG][C::kCpt];
+      bool ok[C::kG];
+#pragma unroll
+      for (int i = 0; i < C::kG; ++i) {
+        const int gb = rel + i * 8;
+        ok[i] = gb + g < end;
+#pragma unroll
+        for (int j = 0; j < C::kCpt; ++j) {
+          kr[i][j] = u32x4{0, 0, 0, 0};
+          vr[i][j] = u32x4{0, 0, 0, 0};
+        }
+        if (gb < end) {  // wave-uniform: the group has at least one valid token
+          const int64_t off = row_offset(wb, gb);
+          if (ok[i]) {
+#pragma unroll
+            for (int j = 0; j < C::kCpt; ++j) kr[i][j] = ld_kv<false>(kbase + off + col(j));
+#pragma unroll
+            for (int j = 0; j < C::kCpt; ++j) vr[i][j] = ld_kv<false>(vbase + off + col(j));
+          }
+        }
+      }
+      float sc[C::kG];
+#pragma unroll
+      for (int i = 0; i < C::kG; ++i) {
+        const float x = score(wq, kr[i]);
+        sc[i] = ok[i] ? x : -INFINITY;
+      }
+      update(wm, wl, wacc, sc, vr, ok);
+    }
+
+    // merge the 8 token groups, then write the output (one partition) or the partial
+    const float M = wave_max(wm);
+    const float f = (wm == -INFINITY) ? 0.f : fast_exp2(wm - M);
+    wl *= f;
+#pragma unroll
+    for (int e = 0; e < C::kEpl; ++e) wacc[e] *= f;
+#pragma unroll
+    for (int x = 8; x < kWave; x <<= 1) {
+      wl += shfl_xor_f(wl, x);
+#pragma unroll
+      for (int e = 0; e < C::kEpl; ++e) wacc[e] += shfl_xor_f(wacc[e], x);
+    }
+    if (g != 0) return;
+    const int64_t row = static_cast<int64_t>(seq) * a.num_heads + h;
+    if (single) {
+      const float inv = 1.f / wl;
+      T* op = static_cast<T*>(a.out) + row * D;
+#pragma unroll
+      for (int j = 0; j < C::kCpt; ++j) {
+        float v[C::kEpc];
+#pragma unroll
+        for (int e = 0; e < C::kEpc; ++e) v[e] = wacc[j * C::kEpc + e] * inv;
+        store_chunk<T>(op + col(j), v);
+      }
+    } else {
+      const int64_t slot = row * a.num_parts_max + part;
+      float* wp = a.ws_acc + slot * D;
+#pragma unroll
+      for (int j = 0; j < C::kCpt; ++j)
+#pragma unroll
+        for (int e4 = 0; e4 < C::kEpc; e4 += 4) {
+          f32x4 v = {wacc[j * C::kEpc + e4], wacc[j * C::kEpc + e4 + 1],
+                     wacc[j * C::kEpc + e4 + 2], wacc[j * C::kEpc + e4 + 3]};
+          st16(wp + col(j) + e4, __builtin_bit_cast(u32x4, v));
+        }
+      if (c == 0) {
+        a.ws_ml[slot * 2] = M;
+        a.ws_ml[slot * 2 + 1] = wl;
+      }
+    }
+  };
+
+  if (!joint) {  // this sequence alone: its table entries and length
+    int wb[C::kTabRegs];
+    int wctx = 0;
+#pragma unroll
+    for (int r = 0; r < C::kTabRegs; ++r) wb[r] = 0;
+#pragma unroll
+    for (int kk = 0; kk < kCap; ++kk) {
+      if (kk == s - lead) {
+        wctx = ctxk[kk];
+#pragma unroll
+        for (int r = 0; r < C::kTabRegs; ++r) wb[r] = blk[kk][r];
+      }
+    }
+    finish(qc[0], m[0], l[0], acc[0], wb, 0, min(wctx - start, P), wctx <= P, s);
+    return;
+  }
+  // each member's tokens past the shared prefix, then its result
+#pragma unroll
+  for (int k = 0; k < kCap; ++k)
+    if (k < nact)
+      finish(qc[k], m[k], l[k], acc[k], blk[k], t, min(ctxk[k] - start, P), ctxk[k] <= P,
+             lead + k);
+}
+
 size_t decode_workspace_bytes(int64_t num_tokens, int64_t num_heads, int64_t head_dim,
                               int64_t max_context_len) {
   const int64_t nparts = workspace_parts(static_cast<int>(max_context_len));
@@ -516,8 +821,64 @@ static hipError_t launch_decode_bs(const DecodeArgs& a, int block_size, int max_
   }
 }
 
+template <int D, int BS, int P, int kCap>
+static hipError_t launch_group_t(const DecodeArgs& a0, int max_context_len, hipStream_t stream) {
+  DecodeArgs a = a0;
+  a.part_size = P;
+  const int nparts = (max_context_len + P - 1) / P;
+  a.num_parts_max = workspace_parts(max_context_len);
+  a.ws_acc = static_cast<float*>(a.workspace);
+  a.ws_ml = a.ws_acc + static_cast<int64_t>(a.num_tokens) * a.num_heads * a.num_parts_max * D;
+  a.heads_per_wg = a.num_heads % kHeadsPerWg == 0 ? kHeadsPerWg : 1;
+  const dim3 grid1(a.num_heads / a.heads_per_wg, a.num_seqs, nparts);
+  hipLaunchKernelGGL((decode_group_kernel<D, BS, P, kCap>), grid1, dim3(kWave * a.heads_per_wg),
+                     0, stream, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || nparts <= 1) return err;
+  hipLaunchKernelGGL((decode_merge_kernel<f16, D>), dim3(a.num_heads, a.num_seqs), dim3(kWave), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+template <int D, int BS, int P>
+static hipError_t launch_group_cap(const DecodeArgs& a, int max_context_len, hipStream_t stream) {
+  if (a.group <= 2) return launch_group_t<D, BS, P, 2>(a, max_context_len, stream);
+  if (a.group <= 4) return launch_group_t<D, BS, P, 4>(a, max_context_len, stream);
+  return launch_group_t<D, BS, P, kMaxDecodeGroup>(a, max_context_len, stream);
+}
+
+// Grouped decode (fp16, no window, no ALiBi, one query per sequence; checked by the caller):
+// the plain kernel's partition choice, kept to 256 or 512 tokens so the members' shared
+// prefixes split into enough partitions.
+template <int D>
+static hipError_t launch_group(const DecodeArgs& a, int block_size, int max_context_len,
+                               hipStream_t stream) {
+  static_assert(kMaxDecodeGroup == 6, "group capacities below are 2, 4 and 6");
+  const bool small = pick_partition(a, block_size, max_context_len) <= 256;
+  switch (block_size) {
+    case 8:
+      return small ? launch_group_cap<D, 8, 256>(a, max_context_len, stream)
+                   : launch_group_cap<D, 8, 512>(a, max_context_len, stream);
+    case 16:
+      return small ? launch_group_cap<D, 16, 256>(a, max_context_len, stream)
+                   : launch_group_cap<D, 16, 512>(a, max_context_len, stream);
+    case 32:
+      return small ? launch_group_cap<D, 32, 256>(a, max_context_len, stream)
+                   : launch_group_cap<D, 32, 512>(a, max_context_len, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int block_size,
                          int max_context_len, hipStream_t stream) {
+  if (a.group > 1) {
+    if (dtype != 1 || a.window != 0 || a.alibi != nullptr || a.q_start_loc != nullptr ||
+        a.group > kMaxDecodeGroup)
+      return hipErrorInvalidValue;
+    if (head_dim == 128) return launch_group<128>(a, block_size, max_context_len, stream);
+    if (head_dim == 64) return launch_group<64>(a, block_size, max_context_len, stream);
+    return hipErrorInvalidValue;
+  }
   if (dtype == 1) {
     if (head_dim == 128) return launch_decode_bs<f16, 128>(a, block_size, max_context_len, stream);
     if (head_dim == 64) return launch_decode_bs<f16, 64>(a, block_size, max_context_len, stream);

@@ -29,6 +29,7 @@ struct DecodeArgs {
   int32_t window;          // sliding window in tokens (0 = none)
   const float* alibi;      // per-head ALiBi slopes [num_heads] or nullptr
   uint32_t flags;          // kDecode* bits
+  int32_t group;           // > 1: consecutive runs of this many sequences may share blocks
   void* workspace;         // caller's scratch (see decode_workspace_bytes)
   // set by the launcher:
   int32_t heads_per_wg;    // waves (one head each) per workgroup
@@ -64,6 +65,10 @@ struct TileArgs {
   float* ws_acc;           // [num_tokens][num_heads][num_parts_max][head_dim]
   float* ws_ml;            // [num_tokens][num_heads][num_parts_max][2] = (max, sum), log2 domain
 };
+
+// Largest sequence group of the grouped decode (fp16, no window, no ALiBi, one query per
+// sequence).
+constexpr int kMaxDecodeGroup = 6;
 
 // Smallest context partition any decode launch uses; sizes the workspace.
 constexpr int kMinPartition = 256;

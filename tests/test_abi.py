@@ -94,6 +94,11 @@ def decode_ext(lib, window=0, alibi=None, flags=0, **kw):
     (dict(window=8, o=None), -1), (dict(alibi=FAKE, D=32), -3), (dict(window=8, mcl=129), -2),
     (dict(flags=2), -3), (dict(flags=1 << 31), -3),
     (dict(flags=1, H=64, S=65535, T=65535, mcl=2048, mb=128), -2),     # 1-D grid too large
+    # grouped decode: group sizes 2..6, fp16 pure decode without window, ALiBi or the hint
+    (dict(flags=7 << 8, dt=1), -3), (dict(flags=16 << 8, dt=1), -3), (dict(flags=2 << 8), -3),
+    (dict(flags=(2 << 8) | 1, dt=1), -3), (dict(flags=2 << 8, dt=1, window=8), -3),
+    (dict(flags=2 << 8, dt=1, alibi=FAKE), -3),
+    (dict(flags=2 << 8, dt=1, qsl=FAKE), -3),
 ])
 def test_decode_ext_rejects(lib, args, code):
     assert decode_ext(lib, **args) == code
