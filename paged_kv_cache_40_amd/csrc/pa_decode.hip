@@ -53,7 +53,7 @@
 #define PA_DECODE_PARTITION 0  // 0: chosen per launch (see pick_partition); else forced
 #endif
 #ifndef PA_DECODE_TRIP_U
-#define PA_DECODE_TRIP_U 0  // 0: 2 iterations per trip (1 when an iteration covers 32 tokens)
+#define PA_DECODE_TRIP_U 0  // iterations per trip (0: one)
 #endif
 #ifndef PA_DECODE_NT_LOADS
 #define PA_DECODE_NT_LOADS 1  // K/V are read once: streaming (non-temporal) loads
@@ -92,7 +92,7 @@ __device__ __forceinline__ u32x4 ld_kv(const void* p) {
   return ld16(p);
 }
 
-template <typename T, int D, int BS, int P>
+template <typename T, int D, int BS, int P, int kTripU = PA_DECODE_TRIP_U>
 struct DecodeCfg {
   static constexpr int kElt = sizeof(T);
   static constexpr int kRow = D * kElt;        // bytes of one head's row of one token
@@ -101,7 +101,7 @@ struct DecodeCfg {
   static constexpr int kTpi = 8 * kR;          // tokens per iteration
   static constexpr int kEpc = 16 / kElt;       // elements per 16-byte chunk
   static constexpr int kEpl = kCpt * kEpc;     // elements (head dims) per lane
-  static constexpr int kU = PA_DECODE_TRIP_U > 0 ? PA_DECODE_TRIP_U : 1;  // iterations per trip
+  static constexpr int kU = kTripU > 0 ? kTripU : 1;  // iterations per trip
   static constexpr int kG = kU * kR;           // token groups per lane per trip
   static constexpr int kTrip = kU * kTpi;      // tokens per trip
   static constexpr int kBlocks = P / BS;       // table entries per partition
@@ -125,6 +125,15 @@ constexpr int kXcds = 8;  // accelerator complex dies of an MI355X
 #define PA_DECODE_XCD_CHUNK 128  // work units per run on one XCD (shared-block mode)
 #endif
 constexpr int kXcdChunk = PA_DECODE_XCD_CHUNK;
+#ifndef PA_DECODE_GROUP_TRIP_U
+#define PA_DECODE_GROUP_TRIP_U 0  // grouped decode: iterations per trip (0: as the plain kernel)
+#endif
+#ifndef PA_DECODE_GROUP_REST_DIV
+#define PA_DECODE_GROUP_REST_DIV 8  // grouped decode: joint only if no member adds > P/this
+#endif
+#ifndef PA_DECODE_GROUP_PARTITION
+#define PA_DECODE_GROUP_PARTITION 0  // grouped decode: 0 = default (512), else 256/512/1024
+#endif
 
 template <typename T, int D, int BS, int P, bool kShared>
 __global__ __launch_bounds__(64 * kHeadsPerWg) PA_DECODE_OCCUPANCY
@@ -450,8 +459,9 @@ template <int D, int BS, int P, int kCap>
 __global__ __launch_bounds__(64 * kHeadsPerWg) PA_DECODE_OCCUPANCY
 void decode_group_kernel(DecodeArgs a) {
   using T = f16;
-  using C = DecodeCfg<T, D, BS, P>;
-  constexpr int kRest = P / 8;  // most tokens past the shared prefix one member may add
+  using C = DecodeCfg<T, D, BS, P, PA_DECODE_GROUP_TRIP_U>;
+  constexpr int kRest = P / PA_DECODE_GROUP_REST_DIV;  // most tokens one member may add past
+                                                       // the shared prefix
   const int hg = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
   const int h = hg * a.heads_per_wg + static_cast<int>(threadIdx.x >> 6);
   if (h >= a.num_heads) return;
@@ -847,24 +857,38 @@ static hipError_t launch_group_cap(const DecodeArgs& a, int max_context_len, hip
   return launch_group_t<D, BS, P, kMaxDecodeGroup>(a, max_context_len, stream);
 }
 
-// Grouped decode (fp16, no window, no ALiBi, one query per sequence; checked by the caller):
-// the plain kernel's partition choice, kept to 256 or 512 tokens so the members' shared
-// prefixes split into enough partitions.
+// Grouped decode partition: the largest of 1024, 512, 256 tokens for which runs x heads x
+// partitions of the longest context reach kGroupTargetWaves, about 1.5 joint waves per SIMD.
+// Measured: 16 runs of 6 samples x 40 heads, contexts ~1,000-1,300, is fastest at 512 (137 us;
+// 256: 159, 1024: 178); 64 runs of 4 beams x 40 heads, contexts 1,024-4,096, at 1024.
+constexpr int64_t kGroupTargetWaves = 1536;
+
+static int pick_group_partition(const DecodeArgs& a, int max_context_len) {
+  if (PA_DECODE_GROUP_PARTITION > 0) return PA_DECODE_GROUP_PARTITION;
+  const int64_t units =
+      static_cast<int64_t>((a.num_seqs + a.group - 1) / a.group) * a.num_heads;
+  int p = 1024;
+  while (p > 256 && units * ((max_context_len + p - 1) / p) < kGroupTargetWaves) p >>= 1;
+  return p;
+}
+
+template <int D, int BS>
+static hipError_t launch_group_p(const DecodeArgs& a, int max_context_len, hipStream_t stream) {
+  const int p = pick_group_partition(a, max_context_len);
+  if (p <= 256) return launch_group_cap<D, BS, 256>(a, max_context_len, stream);
+  if (p <= 512) return launch_group_cap<D, BS, 512>(a, max_context_len, stream);
+  return launch_group_cap<D, BS, 1024>(a, max_context_len, stream);
+}
+
+// Grouped decode (fp16, no window, no ALiBi, one query per sequence; checked by the caller).
 template <int D>
 static hipError_t launch_group(const DecodeArgs& a, int block_size, int max_context_len,
                                hipStream_t stream) {
   static_assert(kMaxDecodeGroup == 6, "group capacities below are 2, 4 and 6");
-  const bool small = pick_partition(a, block_size, max_context_len) <= 256;
   switch (block_size) {
-    case 8:
-      return small ? launch_group_cap<D, 8, 256>(a, max_context_len, stream)
-                   : launch_group_cap<D, 8, 512>(a, max_context_len, stream);
-    case 16:
-      return small ? launch_group_cap<D, 16, 256>(a, max_context_len, stream)
-                   : launch_group_cap<D, 16, 512>(a, max_context_len, stream);
-    case 32:
-      return small ? launch_group_cap<D, 32, 256>(a, max_context_len, stream)
-                   : launch_group_cap<D, 32, 512>(a, max_context_len, stream);
+    case 8: return launch_group_p<D, 8>(a, max_context_len, stream);
+    case 16: return launch_group_p<D, 16>(a, max_context_len, stream);
+    case 32: return launch_group_p<D, 32>(a, max_context_len, stream);
     default: return hipErrorInvalidValue;
   }
 }

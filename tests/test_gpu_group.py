@@ -144,15 +144,17 @@ def test_group_early_divergence_long_tails():
     log("[ok]")
 
 
-def test_group_larger_partitions_sampled():
-    """A batch large enough that the launch picks 512-token partitions (64 sequences x 32 heads,
-    contexts near 4,000): sampled sequences against the oracle."""
-    log("[case] 512-token partitions")
-    rng = np.random.default_rng(14)
-    prompts = list(rng.integers(3500, 4000, size=16))
+@pytest.mark.parametrize("lo,hi,B", [(1500, 2000, 16), (3500, 4000, 8)])
+def test_group_larger_partitions_sampled(lo, hi, B):
+    """Batches large enough for longer partitions (16 runs of 4 x 32 heads = 512 joint units):
+    contexts up to ~2,000 take 512-token partitions, up to ~4,000 take 1024-token ones (with
+    B = 8: 128 table entries, two per lane).  Sampled sequences against the oracle."""
+    log(f"[case] longer partitions: prompts U{{{lo}..{hi}}} B={B}")
+    rng = np.random.default_rng(lo + B)
+    prompts = list(rng.integers(lo, hi, size=16))
     tails = [list(rng.integers(1, 20, size=4)) for _ in prompts]
-    b = _runs_batch(prompts, tails, 16, 32, 64, seed=14)
-    _check(*b, 4, "P=512", seqs=[0, 1, 2, 3, 29, 62, 63])
+    b = _runs_batch(prompts, tails, B, 32, 64, seed=lo + B)
+    _check(*b, 4, f"prompts U{{{lo}..{hi}}}", seqs=[0, 1, 2, 3, 29, 62, 63])
     log("[ok]")
 
 
