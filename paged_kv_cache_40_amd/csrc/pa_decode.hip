@@ -126,7 +126,7 @@ constexpr int kXcds = 8;  // accelerator complex dies of an MI355X
 #endif
 constexpr int kXcdChunk = PA_DECODE_XCD_CHUNK;
 #ifndef PA_DECODE_GROUP_TRIP_U
-#define PA_DECODE_GROUP_TRIP_U 0  // grouped decode: iterations per trip (0: as the plain kernel)
+#define PA_DECODE_GROUP_TRIP_U 0  // grouped decode: iterations per trip (0: by run capacity)
 #endif
 #ifndef PA_DECODE_GROUP_REST_DIV
 #define PA_DECODE_GROUP_REST_DIV 8  // grouped decode: joint only if no member adds > P/this
@@ -459,7 +459,11 @@ template <int D, int BS, int P, int kCap>
 __global__ __launch_bounds__(64 * kHeadsPerWg) PA_DECODE_OCCUPANCY
 void decode_group_kernel(DecodeArgs a) {
   using T = f16;
-  using C = DecodeCfg<T, D, BS, P, PA_DECODE_GROUP_TRIP_U>;
+  // two iterations per trip for runs of up to 4 (218 VGPRs, still two waves per SIMD): beam
+  // width 4, 0.87 vs 0.89 ms per step; runs of 2 are faster at one (3 waves per SIMD either
+  // way), runs of 6 have no registers left for it
+  using C = DecodeCfg<T, D, BS, P,
+                      PA_DECODE_GROUP_TRIP_U > 0 ? PA_DECODE_GROUP_TRIP_U : (kCap == 4 ? 2 : 1)>;
   constexpr int kRest = P / PA_DECODE_GROUP_REST_DIV;  // most tokens one member may add past
                                                        // the shared prefix
   const int hg = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
