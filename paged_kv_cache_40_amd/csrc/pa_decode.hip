@@ -463,7 +463,7 @@ void decode_group_kernel(DecodeArgs a) {
   // width 4, 0.87 vs 0.89 ms per step; runs of 2 are faster at one (3 waves per SIMD either
   // way), runs of 6 have no registers left for it
   using C = DecodeCfg<T, D, BS, P,
-                      PA_DECODE_GROUP_TRIP_U > 0 ? PA_DECODE_GROUP_TRIP_U : (kCap == 4 ? 2 : 1)>;
+                      (PA_DECODE_GROUP_TRIP_U > 0 ? PA_DECODE_GROUP_TRIP_U : (kCap == 4 ? 2 : 1))>;
   constexpr int kRest = P / PA_DECODE_GROUP_REST_DIV;  // most tokens one member may add past
                                                        // the shared prefix
   const int hg = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
