@@ -459,11 +459,7 @@ template <int D, int BS, int P, int kCap>
 __global__ __launch_bounds__(64 * kHeadsPerWg) PA_DECODE_OCCUPANCY
 void decode_group_kernel(DecodeArgs a) {
   using T = f16;
-  // two iterations per trip for runs of up to 4 (218 VGPRs, still two waves per SIMD): beam
-  // width 4, 0.87 vs 0.89 ms per step; runs of 2 are faster at one (3 waves per SIMD either
-  // way), runs of 6 have no registers left for it
-  using C = DecodeCfg<T, D, BS, P,
-                      (PA_DECODE_GROUP_TRIP_U > 0 ? PA_DECODE_GROUP_TRIP_U : (kCap == 4 ? 2 : 1))>;
+  using C = DecodeCfg<T, D, BS, P, (PA_DECODE_GROUP_TRIP_U > 0 ? PA_DECODE_GROUP_TRIP_U : 1)>;
   constexpr int kRest = P / PA_DECODE_GROUP_REST_DIV;  // most tokens one member may add past
                                                        // the shared prefix
   const int hg = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
@@ -536,7 +532,13 @@ void decode_group_kernel(DecodeArgs a) {
   const T* kbase = static_cast<const T*>(a.k_pool) + static_cast<int64_t>(h) * D;
   const T* vbase = static_cast<const T*>(a.v_pool) + static_cast<int64_t>(h) * D;
 
-  u32x4 qc[kCap][C::kCpt];
+  // the members' query chunks live in LDS, one private copy per lane (no lane reads another's
+  // slot, so no barrier is needed); the registers they free hold the next trip's loads
+  extern __shared__ u32x4 q_lds[];  // [heads_per_wg][kCap][kCpt][64]
+  const int wv = static_cast<int>(threadIdx.x >> 6);
+  auto q_slot = [&](int k, int j) -> u32x4& {
+    return q_lds[((wv * kCap + k) * C::kCpt + j) * kWave + lane];
+  };
   float m[kCap], l[kCap], acc[kCap][C::kEpl];
 #pragma unroll
   for (int k = 0; k < kCap; ++k) {
@@ -544,13 +546,11 @@ void decode_group_kernel(DecodeArgs a) {
     l[k] = 0.f;
 #pragma unroll
     for (int e = 0; e < C::kEpl; ++e) acc[k][e] = 0.f;
-#pragma unroll
-    for (int j = 0; j < C::kCpt; ++j) qc[k][j] = u32x4{0, 0, 0, 0};
     if (k < nact) {
       const T* qp = static_cast<const T*>(a.q) +
                     (static_cast<int64_t>(base_seq + k) * a.num_heads + h) * D;
 #pragma unroll
-      for (int j = 0; j < C::kCpt; ++j) qc[k][j] = ld16(qp + col(j));
+      for (int j = 0; j < C::kCpt; ++j) q_slot(k, j) = ld16(qp + col(j));
     }
   }
 
@@ -598,13 +598,14 @@ void decode_group_kernel(DecodeArgs a) {
     }
   };
 
-  // shared prefix: each row read once, every member updated from it
+  // shared prefix: each row read once, every member updated from it.  Software-pipelined over
+  // two register buffers: the next trip's loads are in flight while a trip is computed (the
+  // loop is bound by one wave's chain of trips, so latency and arithmetic must overlap).
   if (joint) {
     bool all_ok[C::kG];
 #pragma unroll
     for (int i = 0; i < C::kG; ++i) all_ok[i] = true;
-    for (int rel = 0; rel < t; rel += C::kTrip) {
-      u32x4 kr[C::kG][C::kCpt], vr[C::kG][C::kCpt];
+    auto load_trip = [&](int rel, u32x4 (&kr)[C::kG][C::kCpt], u32x4 (&vr)[C::kG][C::kCpt]) {
       int64_t off[C::kG];
 #pragma unroll
       for (int i = 0; i < C::kG; ++i) {
@@ -616,16 +617,34 @@ void decode_group_kernel(DecodeArgs a) {
       for (int i = 0; i < C::kG; ++i)
 #pragma unroll
         for (int j = 0; j < C::kCpt; ++j) vr[i][j] = ld_kv<false>(vbase + off[i] + col(j));
+    };
+    auto use_trip = [&](const u32x4 (&kr)[C::kG][C::kCpt], const u32x4 (&vr)[C::kG][C::kCpt]) {
 #pragma unroll
       for (int k = 0; k < kCap; ++k) {
         if (k < nact) {
+          u32x4 qk[C::kCpt];
+#pragma unroll
+          for (int j = 0; j < C::kCpt; ++j) qk[j] = q_slot(k, j);
           float sc[C::kG];
 #pragma unroll
-          for (int i = 0; i < C::kG; ++i) sc[i] = score(qc[k], kr[i]);
+          for (int i = 0; i < C::kG; ++i) sc[i] = score(qk, kr[i]);
           update(m[k], l[k], acc[k], sc, vr, all_ok);
         }
       }
+    };
+    const int ntrips = t / C::kTrip;  // >= 1
+    u32x4 ka[C::kG][C::kCpt], va[C::kG][C::kCpt], kb[C::kG][C::kCpt], vb[C::kG][C::kCpt];
+    load_trip(0, ka, va);
+    int trip = 0;
+    for (; trip + 2 <= ntrips; trip += 2) {
+      load_trip((trip + 1) * C::kTrip, kb, vb);
+      use_trip(ka, va);
+      // unconditional, so the wait for buffer b below never covers these loads; when the
+      // trips run out this re-reads the last one, unused
+      load_trip(min(trip + 2, ntrips - 1) * C::kTrip, ka, va);
+      use_trip(kb, vb);
     }
+    if (trip < ntrips) use_trip(ka, va);  // an odd count: the last trip is in buffer a
   }
 
   // one member's own tokens [rel0, end) of the partition (table entries wb), then its result
@@ -738,15 +757,22 @@ void decode_group_kernel(DecodeArgs a) {
         for (int r = 0; r < C::kTabRegs; ++r) wb[r] = blk[kk][r];
       }
     }
-    finish(qc[0], m[0], l[0], acc[0], wb, 0, min(wctx - start, P), wctx <= P, s);
+    u32x4 wq[C::kCpt];
+#pragma unroll
+    for (int j = 0; j < C::kCpt; ++j) wq[j] = q_slot(0, j);
+    finish(wq, m[0], l[0], acc[0], wb, 0, min(wctx - start, P), wctx <= P, s);
     return;
   }
   // each member's tokens past the shared prefix, then its result
 #pragma unroll
   for (int k = 0; k < kCap; ++k)
-    if (k < nact)
-      finish(qc[k], m[k], l[k], acc[k], blk[k], t, min(ctxk[k] - start, P), ctxk[k] <= P,
+    if (k < nact) {
+      u32x4 wq[C::kCpt];
+#pragma unroll
+      for (int j = 0; j < C::kCpt; ++j) wq[j] = q_slot(k, j);
+      finish(wq, m[k], l[k], acc[k], blk[k], t, min(ctxk[k] - start, P), ctxk[k] <= P,
              lead + k);
+    }
 }
 
 size_t decode_workspace_bytes(int64_t num_tokens, int64_t num_heads, int64_t head_dim,
@@ -845,8 +871,9 @@ static hipError_t launch_group_t(const DecodeArgs& a0, int max_context_len, hipS
   a.ws_ml = a.ws_acc + static_cast<int64_t>(a.num_tokens) * a.num_heads * a.num_parts_max * D;
   a.heads_per_wg = a.num_heads % kHeadsPerWg == 0 ? kHeadsPerWg : 1;
   const dim3 grid1(a.num_heads / a.heads_per_wg, a.num_seqs, nparts);
+  const size_t q_bytes = static_cast<size_t>(a.heads_per_wg) * kCap * (D * 2 / 128) * kWave * 16;
   hipLaunchKernelGGL((decode_group_kernel<D, BS, P, kCap>), grid1, dim3(kWave * a.heads_per_wg),
-                     0, stream, a);
+                     q_bytes, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nparts <= 1) return err;
   hipLaunchKernelGGL((decode_merge_kernel<f16, D>), dim3(a.num_heads, a.num_seqs), dim3(kWave), 0,
