@@ -439,8 +439,9 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   for (int i = 0; i < kPer; ++i) op[i] = static_cast<T>(o[i] * inv);
 }
 
-// Grouped decode [P1 sec. 6: the samples of one prompt and the beams of one search share
-// their leading blocks; P2 "並列サンプリングとビームサーチ"].  When the caller places such
+// Grouped decode [P1 sec. 6, parallel-sampling and beam-search paragraphs: the samples of
+// one prompt share its blocks, beam candidates share their common ancestry].  When the caller
+// places such
 // sequences next to each other, in runs of G, the shared rows need only be read once for
 // the whole run.  Partitions are fixed (tokens [p*P, (p+1)*P)), so the members' partitions
 // line up.  For each (run, partition) every wave of the run works out, from the members'
