@@ -119,17 +119,19 @@ def malformed_check(w, decode_seqs, chunk_seqs):
     api.pa_copy_blocks(kp, vp, pairs_d)
     if w.num_writes:
         api.pa_write_kv(kp, vp, t["k_new"], t["v_new"], bt_d, lens_d, t["write_start_loc"])
-    variants = [("plain", 0, None, False), ("shared", 0, None, True),
-                ("window+alibi", 48, _slopes(H), False)]
+    variants = [("plain", 0, None, False, 0), ("shared", 0, None, True, 0),
+                ("window+alibi", 48, _slopes(H), False, 0)]
+    if w.dtype == "f16" and w.q_start_loc() is None:
+        variants.append(("grouped", 0, None, False, 3))  # runs of 3 over broken and intact
     outs = []
-    for name, window, alibi, shared in variants:
+    for name, window, alibi, shared, group in variants:
         obuf, out = _guarded_like(torch.empty_like(t["q"]), 1, 1, GUARD_VALUE)
         obuf.fill_(GUARD_VALUE)
         slopes = None if alibi is None else torch.from_numpy(alibi).cuda()
         api.pa_decode_ext(out, t["q"], kp, vp, bt_d, lens_d, t["q_start_loc"],
                           max_context_len=w.max_context_len, max_query_len=w.max_query_len,
                           workspace=ws, sliding_window=window, alibi_slopes=slopes,
-                          shared_blocks=shared)
+                          shared_blocks=shared, group=group)
         outs.append((name, window, alibi, obuf, out))
     torch.cuda.synchronize()
     log("[ran] library calls returned PA_OK")
