@@ -275,6 +275,14 @@ def bench_config(args) -> int:
                           sliding_window=args.window, alibi_slopes=slopes, group=group)
 
     wall_ms, ev_ms = _timed(step, args.steps, args.warmup)
+
+    def attend():  # the attention call alone, on the pools as the step leaves them
+        api.pa_decode_ext(out, t["q"], t["k_pool"], t["v_pool"], t["block_tables"],
+                          t["context_lens"], t["q_start_loc"], max_context_len=w.max_context_len,
+                          max_query_len=w.max_query_len, workspace=ws, shared_blocks=shared,
+                          sliding_window=args.window, alibi_slopes=slopes, group=group)
+
+    _, attend_ms = _timed(attend, args.steps, args.warmup)
     # the same step after a 1 GiB buffer (4x the 256 MB last-level cache) is rewritten
     scratch = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
     flushed_ms = _timed_flushed(step, args.steps, args.warmup, scratch)
@@ -306,6 +314,17 @@ def bench_config(args) -> int:
         "pct_hbm_peak_logical": round(100 * kv / (wall_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "seq_heads_per_s": round(w.num_seqs * w.num_heads / (wall_ms * 1e-3), 1),
         "kv_memory": kv_memory(w),
+        # pa_decode_ext alone (HIP events, median of back-to-back calls, so a batch smaller
+        # than a few times the 256 MB last-level cache is partly served from it): the K/V
+        # bytes of the distinct blocks read (a shared block counts once: what HBM must
+        # deliver) over its time, against the 8 TB/s HBM peak; not given with a window,
+        # where blocks are read only in part
+        "attention": {"event_ms": round(attend_ms, 4),
+                      "GBs_logical": round(kv / (attend_ms * 1e-3) / 1e9, 2),
+                      "GBs_distinct_blocks": None if args.window else
+                      round(unique / (attend_ms * 1e-3) / 1e9, 2),
+                      "frac_hbm_peak_distinct_blocks": None if args.window else
+                      round(unique / (attend_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
     if w.max_query_len > 1:
         qh = w.num_queries * w.num_heads
