@@ -176,8 +176,8 @@ int pa_decode(void* out, const void* q,
  *   the whole run (P1 sec. 6).  The result is the same attention whatever the
  *   tables hold (the runs only say where to look for sharing); the context
  *   partitions differ from the plain kernel's, so outputs agree with it within
- *   rounding, not bit for bit.  Built for dtype PA_F16 with q_start_loc NULL,
- *   sliding_window 0 and alibi_slopes NULL, and not combined with
+ *   rounding, not bit for bit.  Built for dtype PA_F16 with q_start_loc NULL
+ *   and sliding_window 0 (ALiBi slopes allowed), and not combined with
  *   PA_DECODE_SHARED_BLOCKS: other uses return PA_ERR_UNSUPPORTED.  g = 0 or 1
  *   means no runs.  Choosing between the two: the grouped decode gives each run's
  *   shared rows to one wave, so it needs enough runs to fill the GPU; when

@@ -250,7 +250,7 @@ def pa_decode_ext(out, q, k_pool, v_pool, block_tables, context_lens, q_start_lo
     neighbouring sequences share blocks).  group = g in 2..6: sequences come in runs of g
     whose members may share leading blocks (samples of one prompt, beams of one search); rows
     every member of a run holds in the same blocks are read once for the run (fp16, one query
-    per sequence, no window or ALiBi, not with shared_blocks)."""
+    per sequence, no window, not with shared_blocks; ALiBi slopes allowed)."""
     nb, bs, h, d, dt = _check_pool(k_pool, v_pool)
     S = context_lens.shape[0]
     T = q.shape[0]

@@ -152,8 +152,7 @@ int pa_decode_ext(void* out, const void* q, const void* k_pool, const void* v_po
     return PA_ERR_UNSUPPORTED;
   const int group = static_cast<int>((flags & group_bits) >> PA_DECODE_GROUP_SHIFT);
   if (group > 1 && (group > pa::kMaxDecodeGroup || (flags & PA_DECODE_SHARED_BLOCKS) ||
-                    dtype != PA_F16 || q_start_loc != nullptr || sliding_window != 0 ||
-                    alibi_slopes != nullptr))
+                    dtype != PA_F16 || q_start_loc != nullptr || sliding_window != 0))
     return PA_ERR_UNSUPPORTED;
   if (num_seqs <= 0 || num_tokens <= 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
   if (max_context_len <= 0 || max_query_len <= 0 || max_query_len > max_context_len)

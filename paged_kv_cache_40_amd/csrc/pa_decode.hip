@@ -456,7 +456,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
 // every (sequence, head, partition) is computed exactly once whatever the tables hold: the
 // grouping only says where sharing is likely.  Partials use the plain kernel's workspace
 // slots and merge pass.
-template <int D, int BS, int P, int kCap>
+template <int D, int BS, int P, int kCap, bool kAlibi>
 __global__ __launch_bounds__(64 * kHeadsPerWg) PA_DECODE_OCCUPANCY
 void decode_group_kernel(DecodeArgs a) {
   using T = f16;
@@ -568,11 +568,17 @@ void decode_group_kernel(DecodeArgs a) {
     }
     return (static_cast<int64_t>(id) * BS + (group_base % BS) + g) * row_stride;
   };
-  auto score = [&](const u32x4 (&qv)[C::kCpt], const u32x4 (&kr)[C::kCpt]) {
+  // ALiBi (a compile-time variant: its registers would cost the plain runs a wave per SIMD
+  // at capacity 4): slope * (j - p) added to the score of token j for the member whose
+  // query sits at position p, dist = j - p (log2 units here)
+  const float slope = kAlibi ? a.alibi[h] * kLog2e : 0.f;
+  auto score = [&](const u32x4 (&qv)[C::kCpt], const u32x4 (&kr)[C::kCpt], int dist) {
     float d = 0.f;
 #pragma unroll
     for (int j = 0; j < C::kCpt; ++j) d = chunk_dot<T>(qv[j], kr[j], d);
-    return group_sum<8>(d) * a.scale_log2;
+    const float x = group_sum<8>(d) * a.scale_log2;
+    if constexpr (kAlibi) return fmaf(slope, static_cast<float>(dist), x);
+    return x;
   };
   auto update = [&](float& mk, float& lk, float (&ak)[C::kEpl], const float (&sc)[C::kG],
                     const u32x4 (&vr)[C::kG][C::kCpt], const bool (&ok)[C::kG]) {
@@ -619,7 +625,8 @@ void decode_group_kernel(DecodeArgs a) {
 #pragma unroll
         for (int j = 0; j < C::kCpt; ++j) vr[i][j] = ld_kv<false>(vbase + off[i] + col(j));
     };
-    auto use_trip = [&](const u32x4 (&kr)[C::kG][C::kCpt], const u32x4 (&vr)[C::kG][C::kCpt]) {
+    auto use_trip = [&](const u32x4 (&kr)[C::kG][C::kCpt], const u32x4 (&vr)[C::kG][C::kCpt],
+                        int rel) {
 #pragma unroll
       for (int k = 0; k < kCap; ++k) {
         if (k < nact) {
@@ -628,7 +635,8 @@ void decode_group_kernel(DecodeArgs a) {
           for (int j = 0; j < C::kCpt; ++j) qk[j] = q_slot(k, j);
           float sc[C::kG];
 #pragma unroll
-          for (int i = 0; i < C::kG; ++i) sc[i] = score(qk, kr[i]);
+          for (int i = 0; i < C::kG; ++i)
+            sc[i] = score(qk, kr[i], start + rel + i * 8 + g - (ctxk[k] - 1));
           update(m[k], l[k], acc[k], sc, vr, all_ok);
         }
       }
@@ -639,18 +647,19 @@ void decode_group_kernel(DecodeArgs a) {
     int trip = 0;
     for (; trip + 2 <= ntrips; trip += 2) {
       load_trip((trip + 1) * C::kTrip, kb, vb);
-      use_trip(ka, va);
+      use_trip(ka, va, trip * C::kTrip);
       // unconditional, so the wait for buffer b below never covers these loads; when the
       // trips run out this re-reads the last one, unused
       load_trip(min(trip + 2, ntrips - 1) * C::kTrip, ka, va);
-      use_trip(kb, vb);
+      use_trip(kb, vb, (trip + 1) * C::kTrip);
     }
-    if (trip < ntrips) use_trip(ka, va);  // an odd count: the last trip is in buffer a
+    if (trip < ntrips) use_trip(ka, va, trip * C::kTrip);  // odd count: last trip in buffer a
   }
 
   // one member's own tokens [rel0, end) of the partition (table entries wb), then its result
   auto finish = [&](const u32x4 (&wq)[C::kCpt], float& wm, float& wl, float (&wacc)[C::kEpl],
-                    const int (&wb)[C::kTabRegs], int rel0, int end, bool single, int seq) {
+                    const int (&wb)[C::kTabRegs], int rel0, int end, bool single, int seq,
+                    int qpos) {  // qpos: the member's query position, context length - 1
     int rel = rel0;
     for (; rel + C::kTrip <= end; rel += C::kTrip) {
       u32x4 kr[C::kG][C::kCpt], vr[C::kG][C::kCpt];
@@ -669,7 +678,7 @@ void decode_group_kernel(DecodeArgs a) {
         for (int j = 0; j < C::kCpt; ++j) vr[i][j] = ld_kv<false>(vbase + off[i] + col(j));
       float sc[C::kG];
 #pragma unroll
-      for (int i = 0; i < C::kG; ++i) sc[i] = score(wq, kr[i]);
+      for (int i = 0; i < C::kG; ++i) sc[i] = score(wq, kr[i], start + rel + i * 8 + g - qpos);
       update(wm, wl, wacc, sc, vr, ok);
     }
     if (rel < end) {  // ragged last trip: lanes past the end load nothing
@@ -697,7 +706,7 @@ void decode_group_kernel(DecodeArgs a) {
       float sc[C::kG];
 #pragma unroll
       for (int i = 0; i < C::kG; ++i) {
-        const float x = score(wq, kr[i]);
+        const float x = score(wq, kr[i], start + rel + i * 8 + g - qpos);
         sc[i] = ok[i] ? x : -INFINITY;
       }
       update(wm, wl, wacc, sc, vr, ok);
@@ -761,7 +770,7 @@ void decode_group_kernel(DecodeArgs a) {
     u32x4 wq[C::kCpt];
 #pragma unroll
     for (int j = 0; j < C::kCpt; ++j) wq[j] = q_slot(0, j);
-    finish(wq, m[0], l[0], acc[0], wb, 0, min(wctx - start, P), wctx <= P, s);
+    finish(wq, m[0], l[0], acc[0], wb, 0, min(wctx - start, P), wctx <= P, s, wctx - 1);
     return;
   }
   // each member's tokens past the shared prefix, then its result
@@ -772,7 +781,7 @@ void decode_group_kernel(DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < C::kCpt; ++j) wq[j] = q_slot(k, j);
       finish(wq, m[k], l[k], acc[k], blk[k], t, min(ctxk[k] - start, P), ctxk[k] <= P,
-             lead + k);
+             lead + k, ctxk[k] - 1);
     }
 }
 
@@ -862,7 +871,7 @@ static hipError_t launch_decode_bs(const DecodeArgs& a, int block_size, int max_
   }
 }
 
-template <int D, int BS, int P, int kCap>
+template <int D, int BS, int P, int kCap, bool kAlibi>
 static hipError_t launch_group_t(const DecodeArgs& a0, int max_context_len, hipStream_t stream) {
   DecodeArgs a = a0;
   a.part_size = P;
@@ -873,8 +882,8 @@ static hipError_t launch_group_t(const DecodeArgs& a0, int max_context_len, hipS
   a.heads_per_wg = a.num_heads % kHeadsPerWg == 0 ? kHeadsPerWg : 1;
   const dim3 grid1(a.num_heads / a.heads_per_wg, a.num_seqs, nparts);
   const size_t q_bytes = static_cast<size_t>(a.heads_per_wg) * kCap * (D * 2 / 128) * kWave * 16;
-  hipLaunchKernelGGL((decode_group_kernel<D, BS, P, kCap>), grid1, dim3(kWave * a.heads_per_wg),
-                     q_bytes, stream, a);
+  hipLaunchKernelGGL((decode_group_kernel<D, BS, P, kCap, kAlibi>), grid1,
+                     dim3(kWave * a.heads_per_wg), q_bytes, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nparts <= 1) return err;
   hipLaunchKernelGGL((decode_merge_kernel<f16, D>), dim3(a.num_heads, a.num_seqs), dim3(kWave), 0,
@@ -882,11 +891,17 @@ static hipError_t launch_group_t(const DecodeArgs& a0, int max_context_len, hipS
   return hipGetLastError();
 }
 
+template <int D, int BS, int P, bool kAlibi>
+static hipError_t launch_group_cap(const DecodeArgs& a, int max_context_len, hipStream_t stream) {
+  if (a.group <= 2) return launch_group_t<D, BS, P, 2, kAlibi>(a, max_context_len, stream);
+  if (a.group <= 4) return launch_group_t<D, BS, P, 4, kAlibi>(a, max_context_len, stream);
+  return launch_group_t<D, BS, P, kMaxDecodeGroup, kAlibi>(a, max_context_len, stream);
+}
+
 template <int D, int BS, int P>
 static hipError_t launch_group_cap(const DecodeArgs& a, int max_context_len, hipStream_t stream) {
-  if (a.group <= 2) return launch_group_t<D, BS, P, 2>(a, max_context_len, stream);
-  if (a.group <= 4) return launch_group_t<D, BS, P, 4>(a, max_context_len, stream);
-  return launch_group_t<D, BS, P, kMaxDecodeGroup>(a, max_context_len, stream);
+  if (a.alibi != nullptr) return launch_group_cap<D, BS, P, true>(a, max_context_len, stream);
+  return launch_group_cap<D, BS, P, false>(a, max_context_len, stream);
 }
 
 // Grouped decode partition: the largest of 1024, 512, 256 tokens for which runs x heads x
@@ -912,7 +927,7 @@ static hipError_t launch_group_p(const DecodeArgs& a, int max_context_len, hipSt
   return launch_group_cap<D, BS, 1024>(a, max_context_len, stream);
 }
 
-// Grouped decode (fp16, no window, no ALiBi, one query per sequence; checked by the caller).
+// Grouped decode (fp16, no window, one query per sequence; checked by the caller).
 template <int D>
 static hipError_t launch_group(const DecodeArgs& a, int block_size, int max_context_len,
                                hipStream_t stream) {
@@ -928,8 +943,7 @@ static hipError_t launch_group(const DecodeArgs& a, int block_size, int max_cont
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int block_size,
                          int max_context_len, hipStream_t stream) {
   if (a.group > 1) {
-    if (dtype != 1 || a.window != 0 || a.alibi != nullptr || a.q_start_loc != nullptr ||
-        a.group > kMaxDecodeGroup)
+    if (dtype != 1 || a.window != 0 || a.q_start_loc != nullptr || a.group > kMaxDecodeGroup)
       return hipErrorInvalidValue;
     if (head_dim == 128) return launch_group<128>(a, block_size, max_context_len, stream);
     if (head_dim == 64) return launch_group<64>(a, block_size, max_context_len, stream);

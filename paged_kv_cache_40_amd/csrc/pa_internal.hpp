@@ -66,7 +66,7 @@ struct TileArgs {
   float* ws_ml;            // [num_tokens][num_heads][num_parts_max][2] = (max, sum), log2 domain
 };
 
-// Largest sequence group of the grouped decode (fp16, no window, no ALiBi, one query per
+// Largest sequence group of the grouped decode (fp16, no window, one query per
 // sequence).
 constexpr int kMaxDecodeGroup = 6;
 

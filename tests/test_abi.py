@@ -97,7 +97,6 @@ def decode_ext(lib, window=0, alibi=None, flags=0, **kw):
     # grouped decode: group sizes 2..6, fp16 pure decode without window, ALiBi or the hint
     (dict(flags=7 << 8, dt=1), -3), (dict(flags=16 << 8, dt=1), -3), (dict(flags=2 << 8), -3),
     (dict(flags=(2 << 8) | 1, dt=1), -3), (dict(flags=2 << 8, dt=1, window=8), -3),
-    (dict(flags=2 << 8, dt=1, alibi=FAKE), -3),
     (dict(flags=2 << 8, dt=1, qsl=FAKE), -3),
 ])
 def test_decode_ext_rejects(lib, args, code):

@@ -183,8 +183,7 @@ def test_group_unsupported_uses_rejected():
     cl = torch.tensor(lens, dtype=torch.int32).cuda()
     out = torch.empty_like(q).cuda()
     qd = q.cuda()
-    bad = [dict(group=7), dict(group=2, sliding_window=16), dict(group=2, shared_blocks=True),
-           dict(group=2, alibi_slopes=torch.ones(2, dtype=torch.float32, device="cuda"))]
+    bad = [dict(group=7), dict(group=2, sliding_window=16), dict(group=2, shared_blocks=True)]
     for kw in bad:
         with pytest.raises(RuntimeError, match="status -3"):
             api.pa_decode_ext(out, qd, kpd, vpd, bt, cl, max_context_len=max(lens), **kw)
@@ -242,3 +241,27 @@ def test_group_graph_capture_replays():
         ref = paged_attention_seq(q.numpy()[s_:s_ + 1], kn, vn, np.asarray(tables[s_]), lens[s_], 16)
         assert_close(eager[s_:s_ + 1].cpu().numpy(), ref, "f16", f"graph seq {s_}")
     log("[ok] 4 replays bit-identical")
+
+
+@pytest.mark.parametrize("group,D,B", [(6, 128, 16), (4, 64, 8), (2, 128, 32)])
+def test_group_alibi_matches_oracle(group, D, B):
+    """ALiBi with runs: slope_h * (j - p) with each member's own query position p, on the
+    geometric slopes 2^-2 .. 2^-8 (the steepest makes attention local, so a wrong p shows)."""
+    log(f"[case] grouped decode + ALiBi group={group} d={D} B={B}")
+    rng = np.random.default_rng(31 + group)
+    H = 4
+    tails = [list(rng.integers(1, 300, size=group)) for _ in range(3)]
+    q, kp, vp, tables, lens = _runs_batch([1000, 700, 1300], tails, B, H, D, seed=31 + group)
+    slopes = (2.0 ** (-8.0 * (np.arange(H) + 1) / H)).astype(np.float32)
+    kpd, vpd = kp.cuda(), vp.cuda()
+    sl = torch.from_numpy(slopes).cuda()
+    out = _run(q, kpd, vpd, tables, lens, group, alibi_slopes=sl)
+    plain = _run(q, kpd, vpd, tables, lens, 0, alibi_slopes=sl)
+    kn, vn, qn = kp.numpy(), vp.numpy(), q.numpy()
+    for s in range(len(lens)):
+        ref = paged_attention_seq(qn[s:s + 1], kn, vn, np.asarray(tables[s]), lens[s], B,
+                                  alibi_slopes=slopes.astype(np.float64))
+        assert_close(out[s:s + 1].numpy(), ref, "f16", f"alibi seq {s}")
+    p, gr = plain.double().numpy(), out.double().numpy()
+    assert (np.abs(gr - p) <= 2 * (2e-3 + 1e-2 * np.abs(p))).all()
+    log("[ok]")
