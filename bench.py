@@ -252,7 +252,7 @@ def bench_config(args) -> int:
     if group is None:
         runs = int(w.extra.get("samples", 0))
         group = runs if 2 <= runs <= 6 and w.dtype == "f16" and not (
-            args.window or args.alibi or args.no_shared_hint) else 0
+            args.window or args.no_shared_hint) else 0
         # too few joint units to fill the chip (e.g. one GPU's share of the heads): the
         # shared-blocks hint is faster there (16 runs x 5 heads: 0.083 vs 0.107 ms per step)
         if group and -(-w.num_seqs // group) * w.num_heads * -(-w.max_context_len // 256) < 1536:
