@@ -530,6 +530,7 @@ def bench_beam(args) -> int:
                           workspace=ws, shared_blocks=not (args.no_shared_hint or group),
                           group=group)
 
+    kp0, vp0 = kp.clone(), vp.clone()  # the pools after the prefill, for the graph replays
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
     t0 = time.perf_counter()
@@ -539,6 +540,32 @@ def bench_beam(args) -> int:
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     ev_ms = ev0.elapsed_time(ev1) / steps
+    # the same plan captured once in a HIP graph and replayed from the post-prefill pools
+    # (pruned beams' blocks are reused by others, so a replay must start where the eager
+    # pass started): the GPU time of the steps without the host issuing each call, and the
+    # last step's output, which must equal the eager one bit for bit
+    eager_last = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for d in dev:
+            run_step(d)
+    graph_times, graph_same = [], True
+    for _ in range(2):
+        kp.copy_(kp0)
+        vp.copy_(vp0)
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_times.append(g0.elapsed_time(g1) / steps)
+        graph_same &= bool(torch.equal(out.view(torch.int16), eager_last.view(torch.int16)))
+    graph_ms = min(graph_times)
+    del graph, kp0, vp0
     logical = int(sum(2 * int(lens.astype(np.int64).sum()) * H * D * 2 for _, _, lens in plan))
     unique = int(sum(2 * held * B * H * D * 2 for held, _, _ in savings))
     copies = int(sum(len(p) for p, _, _ in plan))
@@ -553,6 +580,8 @@ def bench_beam(args) -> int:
                    "shared_blocks_hint": not (args.no_shared_hint or group),
                    "group": group},
         "wall_ms_per_step": round(wall_ms, 4),
+        "graph_ms_per_step": round(graph_ms, 4),
+        "graph_output_equals_eager": graph_same,
         "candidate_tokens_per_s": round(R * W / (ev_ms * 1e-3), 1),
         "unique_block_GBs": round(unique / steps / (ev_ms * 1e-3) / 1e9, 2),
         "cow_copies_per_step": round(copies / steps, 2),
