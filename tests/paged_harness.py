@@ -22,18 +22,18 @@ def log(msg: str) -> None:
     print(msg, flush=True)
 
 
-def run_library(w, t, stream=None, workspace=None, window=0, alibi=None, shared=False):
+def run_library(w, t, stream=None, workspace=None, window=0, alibi=None, shared=False, group=0):
     """copy-on-write copies -> slot writes -> attention, in stream order. Returns out.
 
-    window / alibi (host float slopes [H]) / shared (the shared-blocks hint) select
-    pa_decode_ext."""
+    window / alibi (host float slopes [H]) / shared (the shared-blocks hint) / group (runs of
+    g sequences for the grouped decode) select pa_decode_ext."""
     if w.copy_pairs is not None and len(w.copy_pairs):
         api.pa_copy_blocks(t["k_pool"], t["v_pool"], t["copy_pairs"], stream=stream)
     if w.num_writes:
         api.pa_write_kv(t["k_pool"], t["v_pool"], t["k_new"], t["v_new"], t["block_tables"],
                         t["context_lens"], t["write_start_loc"], stream=stream)
     out = torch.empty_like(t["q"])
-    if window == 0 and alibi is None and not shared:
+    if window == 0 and alibi is None and not shared and not group:
         api.pa_decode(out, t["q"], t["k_pool"], t["v_pool"], t["block_tables"],
                       t["context_lens"], t["q_start_loc"], max_context_len=w.max_context_len,
                       max_query_len=w.max_query_len, workspace=workspace, stream=stream)
@@ -44,7 +44,7 @@ def run_library(w, t, stream=None, workspace=None, window=0, alibi=None, shared=
                           t["context_lens"], t["q_start_loc"], max_context_len=w.max_context_len,
                           max_query_len=w.max_query_len, workspace=workspace,
                           sliding_window=window, alibi_slopes=slopes, shared_blocks=shared,
-                          stream=stream)
+                          stream=stream, group=group)
     return out
 
 
@@ -52,10 +52,24 @@ def host_copy(t: dict) -> dict:
     return {k: (None if v is None else v.cpu().numpy()) for k, v in t.items()}
 
 
+def assert_fp32_inputs_full(h: dict, what: str = "") -> None:
+    """fp32 parity runs on full-mantissa inputs: almost every finite value of q, K and V must
+    change when rounded to fp16, so a path that went through fp16 cannot meet 1e-5."""
+    for name in ("q", "k_pool", "v_pool"):
+        a = np.asarray(h[name])
+        if a.dtype != np.float32:
+            return
+        a = a[np.isfinite(a)]
+        frac = float(np.mean(a.astype(np.float16).astype(np.float32) != a)) if a.size else 1.0
+        assert frac > 0.99, f"{what}: fp32 {name} is fp16-exact in {1 - frac:.1%} of values"
+
+
 def oracle_step(w, h: dict, window=0, alibi=None):
     """The oracle's copy -> write -> attention on host arrays. Returns (out, k_pool, v_pool).
 
-    alibi slopes are taken as the float32 values the library receives."""
+    alibi slopes are taken as the float32 values the library receives.  fp32 inputs must be
+    full-mantissa (assert_fp32_inputs_full)."""
+    assert_fp32_inputs_full(h, w.name)
     kp, vp = h["k_pool"], h["v_pool"]
     if w.copy_pairs is not None and len(w.copy_pairs):
         kp, vp = oracle.copy_blocks(kp, vp, h["copy_pairs"])
@@ -174,6 +188,108 @@ def oracle_sub(w, sub, heads=None, window=0, alibi=None):
                                                w.block_size, heads=heads, window=window,
                                                alibi_slopes=_slopes64(alibi)))
     return outs, kp[:-1], vp[:-1]
+
+
+def _apply_step_in_place(w, sub) -> None:
+    """The oracle's copy-on-write copies, then slot writes, applied to the compact host pools of
+    `sub` (a snapshot_for() of the batch), touching only the blocks involved: both oracle
+    functions run on a small pool of those blocks, which is then put back."""
+    B = w.block_size
+    kp, vp = sub["k_pool"], sub["v_pool"]
+    pairs = sub["copy_pairs"]
+    if len(pairs):
+        mini = np.unique(pairs.reshape(-1))
+        pos = {int(b): i for i, b in enumerate(mini)}
+        local = np.asarray([(pos[int(a)], pos[int(b)]) for a, b in pairs], np.int32)
+        ck, cv = oracle.copy_blocks(kp[mini], vp[mini], local)
+        kp[mini], vp[mini] = ck, cv
+    if w.num_writes:
+        bt, cl, wsl = sub["block_tables"], sub["context_lens"], sub["write_start_loc"]
+        S = len(cl)
+        wsl = np.arange(S + 1) if wsl is None else wsl
+        written = sorted({int(bt[s, (int(cl[s]) - (int(wsl[s + 1]) - int(wsl[s])) + i) // B])
+                          for s in range(S) for i in range(int(wsl[s + 1]) - int(wsl[s]))})
+        mini = np.asarray(written, np.int64)
+        pos = np.zeros(kp.shape[0], np.int32)
+        pos[mini] = np.arange(len(mini), dtype=np.int32)
+        local_bt = pos[np.maximum(bt, 0)].astype(np.int32)     # unwritten entries never used
+        wk, wv = oracle.write_kv(kp[mini], vp[mini], sub["k_new"], sub["v_new"], local_bt, cl,
+                                 B, wsl)
+        kp[mini], vp[mini] = wk, wv
+
+
+def oracle_every_sequence(w, sub, window=0, alibi=None, margins=False):
+    """The oracle's step (copies, writes, attention) for every sequence of a compact snapshot
+    (snapshot_for over all sequences), attention in a pool of host processes.  Returns
+    ({sequence: [n_s][H][d]}, {sequence: smallest drop-one-block margin}) - the margins (see
+    tests/sensitivity.py) only when asked, for decode sequences longer than one block."""
+    from oracle_pool import attention_all
+    _apply_step_in_place(w, sub)
+    n = sub["num_attn"]
+    outs, m = attention_all(sub["k_pool"], sub["v_pool"], sub["block_tables"][:n],
+                            sub["context_lens"][:n], sub["q_start_loc"], sub["q"], w.block_size,
+                            window=window, alibi=_slopes64(alibi),
+                            margins_tol=TOL[w.dtype] if margins else None)
+    return outs, m
+
+
+def moved_slots_check(w, t, k_before, v_before):
+    """Slots that changed anywhere in the pools: exactly the written slots and the filled
+    part of every copied block."""
+    B, S = w.block_size, w.num_seqs
+    itype = torch.int16 if w.dtype == "f16" else torch.int32
+    moved = set()
+    for before, after in ((k_before, t["k_pool"]), (v_before, t["v_pool"])):
+        diff = (before.view(itype) != after.view(itype)).view(w.num_blocks, B, -1).any(-1)
+        moved |= {tuple(x) for x in diff.nonzero().cpu().tolist()}
+    expect = set()
+    wl = w.write_lens
+    for s in range(S):
+        L = int(w.context_lens[s])
+        for i in range(int(wl[s])):
+            p = L - int(wl[s]) + i
+            expect.add((int(w.block_tables[s, p // B]), p % B))
+    if w.copy_pairs is not None:
+        fb = w.filled_before
+        for src, dst in w.copy_pairs:
+            expect |= {(int(dst), j) for j in range(int(fb[src]))}
+    assert moved == expect
+
+
+def every_sequence_check(w, group=0, margins=False, min_margin=3.0):
+    """The full batch as bench.py runs it, every sequence and head against the oracle (in a
+    pool of host processes), the pools bit for bit over every block the batch reads, and a
+    whole-pool check that only the expected slots moved.  With margins, also shows on these
+    very inputs that leaving out any one block of any decode sequence would break the
+    tolerance (tests/sensitivity.py)."""
+    log(f"[case] full {w.name} S={w.num_seqs} H={w.num_heads} NB={w.num_blocks} group={group} "
+        f"k_scale={w.k_scale} v_mark={w.v_mark}")
+    t = w.device_tensors("cuda")
+    seqs = list(range(w.num_seqs))
+    sub = snapshot_for(w, t, seqs)
+    k_before = t["k_pool"].clone()
+    v_before = t["v_pool"].clone()
+    out = run_library(w, t, group=group)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    log("[step] library done; oracle over every sequence")
+    refs, m = oracle_every_sequence(w, sub, margins=margins)
+    worst = 0.0
+    for i, s in enumerate(seqs):
+        worst = max(worst, assert_close(got[sub["q_rows"][i]], refs[s], w.dtype,
+                                        f"{w.name} seq {s}"))
+    idx_t = torch.tensor(sub["uniq"], dtype=torch.int64, device="cuda")
+    assert_bits_equal(t["k_pool"].index_select(0, idx_t).cpu().numpy(), sub["k_pool"][:-1],
+                      "k_pool")
+    assert_bits_equal(t["v_pool"].index_select(0, idx_t).cpu().numpy(), sub["v_pool"][:-1],
+                      "v_pool")
+    moved_slots_check(w, t, k_before, v_before)
+    if margins:
+        assert len(m) > 0
+        low = min(m.values())
+        assert low >= min_margin, f"inputs too blunt: a block moves the output by {low:.2f} tol"
+        log(f"[ok] smallest drop-one-block margin {low:.1f}x the tolerance")
+    log(f"[ok] {len(seqs)} sequences, max abs err {worst:.3g}")
 
 
 def pick_sequences(w, n=4, seed=0):

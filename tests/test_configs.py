@@ -104,3 +104,86 @@ def test_small_variants_host_tensors():
         valid = np.arange(w.block_size)[None, :] < w.filled_before[:, None]
         assert np.isfinite(t["k_pool"][valid]).all() and np.isnan(t["k_pool"][~valid]).all()
         assert t["q"].shape == (w.num_queries, w.num_heads, w.head_dim)
+
+
+# ------------------------------------------------------------ value recipes --
+
+def test_full_mantissa_host_and_torch_agree_and_are_not_fp16():
+    from workloads.gen import full_values
+    host = normal_array(9, 4, (7, 3, 64), np.float32, offset=(1 << 32) - 50, full=True)
+    dev = torch.empty((7, 3, 64), dtype=torch.float32)
+    normal_values_torch(9, 4, dev, offset=(1 << 32) - 50, chunk=97, full=True)
+    assert host.tobytes() == dev.numpy().tobytes()
+    x = full_values(1, 1, np.arange(1 << 18), np.float64)
+    # close to the grid value it perturbs, a full fp32 mantissa, almost never exact in fp16
+    base = normal_values(1, 1, np.arange(1 << 18), np.float64)
+    assert np.abs(x - base).max() <= 2.0 ** -9
+    x32 = x.astype(np.float32)
+    assert np.mean(x32.astype(np.float16).astype(np.float32) != x32) > 0.999
+    assert abs(x.mean()) < 1e-2 and abs(x.var() - 1) < 2e-2
+
+
+def test_full_values_only_for_fp32():
+    with pytest.raises(ValueError):
+        make_small(2, values="full")
+    w = make_config(1, values="full")
+    h = w.host_tensors()
+    for name in ("k_pool", "v_pool", "q"):
+        a = h[name][np.isfinite(h[name])]
+        assert np.mean(a.astype(np.float16).astype(np.float32) != a) > 0.99, name
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_marked_values_host_and_torch_agree(dtype):
+    from workloads import make_custom_decode
+    w = make_custom_decode(3, dtype, 3, 64, 16, [1, 17, 40, 100], write_one=True, k_scale=0.125,
+                           v_mark=512.0)
+    h = w.host_tensors()
+    d = w.device_tensors("cpu")
+    for name in ("k_pool", "v_pool", "q", "k_new", "v_new"):
+        a, b = h[name], d[name].numpy()
+        assert a.dtype == b.dtype and a.tobytes() == b.tobytes(), name
+
+
+def test_marked_values_alternate_by_logical_block():
+    from workloads import make_custom_decode
+    w = make_custom_decode(4, "f16", 2, 64, 16, [70, 33], write_one=True, k_scale=0.125,
+                           v_mark=1024.0)
+    h = w.host_tensors()
+    r = w.head_dim_signs()
+    assert set(np.unique(r)) == {-1.0, 1.0}
+    B = w.block_size
+    for s in range(w.num_seqs):
+        L = int(w.context_lens[s])
+        for j in range(L - 1):                      # tokens already in the pool
+            blk = w.block_tables[s, j // B]
+            v = h["v_pool"][blk, j % B].astype(np.float64)
+            want = (1 if (j // B) % 2 == 0 else -1) * 1024.0 * r
+            assert np.abs(v - want).max() <= 8, (s, j)
+        # the appended token carries its own block's sign
+        v = h["v_new"][s].astype(np.float64)
+        want = (1 if ((L - 1) // B) % 2 == 0 else -1) * 1024.0 * B * r
+        assert np.abs(v - want).max() <= 16
+    k = h["k_pool"][np.isfinite(h["k_pool"])]
+    assert np.abs(k).max() <= 6 / 8
+
+
+@pytest.mark.parametrize("recipe", [dict(), dict(k_scale=0.125, v_mark=256.0)])
+def test_host_block_rows_match_whole_pool(recipe):
+    from workloads import make_custom_decode
+    w = make_custom_decode(5, "f16", 3, 64, 16, [5, 40, 100], write_one=True, **recipe)
+    h = w.host_tensors()
+    blocks = [int(w.block_tables[1, 1]), int(w.block_tables[2, 0]), int(w.block_tables[0, 0])]
+    for heads in (None, [2], [0, 2]):
+        r = w.host_block_rows(blocks, heads)
+        sel = slice(None) if heads is None else heads
+        for name in ("k_pool", "v_pool"):
+            want = h[name][blocks][:, :, sel]
+            assert r[name].tobytes() == want.tobytes(), (name, heads)
+    nr = w.host_new_rows([1, 2])
+    assert nr["k_new"].tobytes() == h["k_new"][:, [1, 2]].tobytes()
+    assert nr["v_new"].tobytes() == h["v_new"][:, [1, 2]].tobytes()
+    wf = make_config(1, values="full")
+    hf = wf.host_tensors()
+    r = wf.host_block_rows([3, 7])
+    assert r["v_pool"].tobytes() == hf["v_pool"][[3, 7]].tobytes()

@@ -19,11 +19,14 @@ from paged_harness import assert_close, log
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("grouped", [False, True])
 @pytest.mark.parametrize("width,B", [(4, 16), (6, 8), (2, 32)])
-def test_beam_search_steps_match_dense_history(width, B):
+def test_beam_search_steps_match_dense_history(width, B, grouped):
+    """grouped: each request's beams named as a run of the grouped decode (as bench.py --beam
+    runs them); otherwise the plain decode."""
     H, D, steps = 4, 128, 40
     prompts = [37, 50, 16]
-    log(f"[case] beam width={width} B={B} prompts={prompts} steps={steps}")
+    log(f"[case] beam width={width} B={B} prompts={prompts} steps={steps} grouped={grouped}")
     trees = [make_beam_tree(100 + i, width, steps, P) for i, P in enumerate(prompts)]
     rows = [beam_rows(tr, H, D) for tr in trees]
     qs = [beam_queries(tr, H, D) for tr in trees]
@@ -58,7 +61,10 @@ def test_beam_search_steps_match_dense_history(width, B):
         api.pa_write_kv(kp, vp, kn, vn, bt, cl)
         q = torch.from_numpy(np.concatenate([qq[t] for qq in qs])).cuda()
         out = torch.empty_like(q)
-        api.pa_decode(out, q, kp, vp, bt, cl, max_context_len=int(L.max()))
+        if grouped:
+            api.pa_decode_ext(out, q, kp, vp, bt, cl, max_context_len=int(L.max()), group=width)
+        else:
+            api.pa_decode(out, q, kp, vp, bt, cl, max_context_len=int(L.max()))
         got = out.cpu().numpy()
         row = 0
         for i, tr in enumerate(trees):

@@ -12,7 +12,8 @@ import torch
 
 from oracle.attention import paged_attention_seq
 from paged_kv_cache_40_amd import api
-from paged_harness import assert_close, log
+from paged_harness import assert_close, every_sequence_check, log
+from workloads import make_config
 
 pytestmark = pytest.mark.gpu
 
@@ -265,3 +266,29 @@ def test_group_alibi_matches_oracle(group, D, B):
     p, gr = plain.double().numpy(), out.double().numpy()
     assert (np.abs(gr - p) <= 2 * (2e-3 + 1e-2 * np.abs(p))).all()
     log("[ok]")
+
+
+def test_full_parallel_sampling_batch_grouped_every_sequence():
+    """The parallel-sampling batch exactly as bench.py runs it (16 prompts x 6 samples, 40
+    heads, the copy-on-write copies and the step's writes first), with the runs of 6 named:
+    every sequence and head against the oracle."""
+    every_sequence_check(make_config(3), group=6)
+
+
+@pytest.mark.parametrize("prompt,tail_max", [(1000, 300), (2600, 200)])
+def test_group_runs_of_six_at_forty_heads(prompt, tail_max):
+    """Sixteen runs of six samples x 40 heads at head_dim 128: enough joint units that the
+    launch takes its longer partitions (the shapes bench.py times), every sequence against the
+    oracle in a pool of host processes."""
+    from oracle_pool import attention_all
+    rng = np.random.default_rng(prompt)
+    tails = [list(rng.integers(1, tail_max + 1, size=6)) for _ in range(16)]
+    q, kp, vp, tables, lens = _runs_batch([prompt] * 16, tails, 16, 40, 128, seed=prompt)
+    log(f"[case] 16 runs of 6, prompt {prompt}, 40 heads, max context {max(lens)}")
+    out = _run(q, kp.cuda(), vp.cuda(), tables, lens, 6)
+    refs, _ = attention_all(kp.numpy(), vp.numpy(), np.asarray(tables, np.int32),
+                            np.asarray(lens, np.int32), None, q.numpy(), 16)
+    worst = 0.0
+    for s in range(len(lens)):
+        worst = max(worst, assert_close(out[s:s + 1].numpy(), refs[s], "f16", f"seq {s}"))
+    log(f"[ok] max abs err {worst:.3g}")

@@ -14,8 +14,10 @@ import torch
 import oracle
 from paged_kv_cache_40_amd import api
 from workloads import make_config, make_small, make_custom_decode, make_custom_mixed
-from paged_harness import (assert_bits_equal, assert_close, host_copy, log, oracle_step,
-                           oracle_sub, pick_sequences, run_library, snapshot_for)
+from cases import long_chunk_marked, long_decode_marked
+from paged_harness import (assert_bits_equal, assert_close, every_sequence_check, host_copy, log,
+                           oracle_step, oracle_sub, pick_sequences, run_library, snapshot_for)
+from sensitivity import drop_block_margins, drop_last_token_margin
 
 pytestmark = pytest.mark.gpu
 
@@ -54,45 +56,15 @@ def test_small_config2_peaked(q_scale):
 
 
 @pytest.mark.parametrize("idx", [2, 3, 4, 5])
-def test_full_size_sampled(idx):
-    """The full batch as bench.py runs it; the oracle recomputes sampled sequences (every head)
-    and their blocks of the pools, plus a whole-pool check that only the expected slots moved."""
-    w = make_config(idx)
-    log(f"[case] full {w.name} S={w.num_seqs} NB={w.num_blocks}")
-    t = w.device_tensors("cuda")
-    seqs = pick_sequences(w, n=4, seed=idx)
-    sub = snapshot_for(w, t, seqs)
-    k_before = t["k_pool"].clone()
-    v_before = t["v_pool"].clone()
-    out = run_library(w, t)
-    torch.cuda.synchronize()
-    refs, kp, vp = oracle_sub(w, sub)
-    for i, s in enumerate(seqs):
-        rows = torch.from_numpy(sub["q_rows"][i]).cuda()
-        assert_close(out[rows].cpu().numpy(), refs[i], w.dtype, f"{w.name} seq {s}")
-    idx_t = torch.tensor(sub["uniq"], dtype=torch.int64, device="cuda")
-    assert_bits_equal(t["k_pool"].index_select(0, idx_t).cpu().numpy(), kp, "k_pool sampled")
-    assert_bits_equal(t["v_pool"].index_select(0, idx_t).cpu().numpy(), vp, "v_pool sampled")
-    # slots that changed anywhere in the pool: exactly the written slots and copied blocks
-    B, S = w.block_size, w.num_seqs
-    itype = torch.int16 if w.dtype == "f16" else torch.int32
-    moved = set()
-    for before, after in ((k_before, t["k_pool"]), (v_before, t["v_pool"])):
-        diff = (before.view(itype) != after.view(itype)).view(w.num_blocks, B, -1).any(-1)
-        moved |= {tuple(x) for x in diff.nonzero().cpu().tolist()}
-    expect = set()
-    wl = w.write_lens
-    for s in range(S):
-        L = int(w.context_lens[s])
-        for i in range(int(wl[s])):
-            p = L - int(wl[s]) + i
-            expect.add((int(w.block_tables[s, p // B]), p % B))
-    if w.copy_pairs is not None:
-        fb = w.filled_before
-        for src, dst in w.copy_pairs:
-            expect |= {(int(dst), j) for j in range(int(fb[src]))}
-    assert moved == expect
-    log("[ok]")
+def test_full_size_every_sequence(idx):
+    every_sequence_check(make_config(idx))
+
+
+def test_full_size_large_batch_marked():
+    """The large batch with block-marked values and small keys (workloads.configs: v_mark,
+    k_scale): every sequence against the oracle, on inputs where any one dropped block of any
+    sequence would exceed the tolerance (shown on these inputs by the test itself)."""
+    every_sequence_check(make_config(5, k_scale=0.125, v_mark=2048.0), margins=True)
 
 
 # ------------------------------------------------------- layouts, edges --
@@ -485,6 +457,53 @@ def test_long_contexts():
     full_check(w)
     w = make_custom_mixed(82, 2, 16, [(30000, 300), (5, 40)], [20000, 9], name="long_chunk")
     full_check(w)
+
+
+def _sharpness(w, t_host_after, s, query_rows):
+    """Smallest drop-one-block margin over the whole blocks each of sequence s's queries sees
+    (and the appended token's margin for the last query), on the post-step host pools."""
+    import oracle
+    B = w.block_size
+    L = int(w.context_lens[s])
+    kp, vp = t_host_after
+    keys = oracle.gather_context(kp, w.block_tables[s], L, B)
+    vals = oracle.gather_context(vp, w.block_tables[s], L, B)
+    n = len(query_rows)
+    low = np.inf
+    for i, qrow in enumerate(query_rows):
+        p = L - n + i
+        m = drop_block_margins(qrow, keys[:p + 1], vals[:p + 1], B, 2e-3, 1e-2)
+        low = min(low, (m if n == 1 else m[:(p + 1) // B]).min())
+    last = drop_last_token_margin(query_rows[-1], keys, vals, 2e-3, 1e-2)
+    return low, last
+
+
+def test_long_contexts_marked():
+    """The long contexts on block-marked inputs (tests/cases.py): any one dropped block, the
+    one-token last partition of the 65,537-token decode, or a misordered partition merge
+    would break the tolerance - shown here on these very inputs before comparing."""
+    for w in (long_decode_marked(), long_chunk_marked()):
+        log(f"[case] {w.name}")
+        t = w.device_tensors("cuda")
+        h = host_copy(t)
+        out = run_library(w, t)
+        torch.cuda.synchronize()
+        ref, kp, vp = oracle_step(w, h)
+        assert_close(out.cpu().numpy(), ref, w.dtype, w.name)
+        assert_bits_equal(t["k_pool"].cpu().numpy(), kp, "k_pool")
+        assert_bits_equal(t["v_pool"].cpu().numpy(), vp, "v_pool")
+        qsl = w.q_start_loc()
+        for s in np.flatnonzero(w.context_lens >= 20000):
+            a, b = (s, s + 1) if qsl is None else (int(qsl[s]), int(qsl[s + 1]))
+            rows = h["q"][a:b].astype(np.float64)
+            if b - a > 1:
+                low, last = _sharpness(w, (kp, vp), s, rows)   # every query of the chunk
+            else:
+                low, last = _sharpness(w, (kp, vp), s, rows)
+            log(f"[sharp] seq {s} L={int(w.context_lens[s])}: block margin {low:.1f}, "
+                f"last token {last:.1f}")
+            assert low >= 3.0 and (b - a > 1 or last >= 3.0)
+        log("[ok]")
 
 
 def test_chunk_only_batch():

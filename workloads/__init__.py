@@ -7,7 +7,7 @@ shared); it computes nothing of the attention, the slot write or the block
 copy themselves.
 """
 
-from .gen import normal_values, normal_values_torch, key_for  # noqa: F401
+from .gen import normal_values, normal_values_torch, full_values, key_for  # noqa: F401
 from .configs import (  # noqa: F401
     Workload,
     make_config,

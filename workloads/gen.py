@@ -20,6 +20,15 @@ The value is the Irwin-Hall approximation of N(0, 1) (sum of twelve uniforms
 minus their mean): mean 0, variance 65535/65536, support [-5.98, 5.98].  It is
 a multiple of 1/256 with |numerator| <= 1530 < 2^11, so it is exact in fp16,
 fp32 and fp64 alike; no rounding ever differs between host and device.
+
+Full-mantissa variant (full_values*): a fourth word w_3 adds a 24-bit
+perturbation u = w_3 >> 8 below the 1/256 grid,
+  value = ((S - 1530) * 2^24 + (u - 2^23)) / 2^32,
+an integer over a power of two, exact in fp64 (|numerator| < 2^35).  Cast to
+fp32 it rounds once (to nearest even), so almost every value uses all 24
+mantissa bits and is NOT representable in fp16; host and device round the same
+exact fp64 number and agree bit for bit.  Used for fp32 batches, so that an
+fp32 path that silently went through fp16 would be seen.
 """
 
 from __future__ import annotations
@@ -78,14 +87,34 @@ def normal_values(seed: int, stream: int, index, dtype=np.float32):
     return out.astype(dtype)
 
 
+def full_values(seed: int, stream: int, index, dtype=np.float32):
+    """Full-mantissa values at the given flat indices: the normal value plus a 24-bit
+    perturbation in [-2^-9, 2^-9), as an exact fp64 number rounded once to `dtype`."""
+    idx = np.asarray(index, dtype=np.int64)
+    lo = idx & M32
+    hi = idx >> 32
+    s = np.zeros(idx.shape, dtype=np.int64)
+    for r in range(3):
+        k = key_for(seed, stream, r)
+        w = _mix32_np(_mix32_np(lo ^ k) ^ ((hi * _C3 + k) & M32))
+        s += _byte_sum_np(w)
+    k = key_for(seed, stream, 3)
+    u = _mix32_np(_mix32_np(lo ^ k) ^ ((hi * _C3 + k) & M32)) >> 8
+    num = (s - 1530) * (1 << 24) + (u - (1 << 23))
+    out = num.astype(np.float64) / float(1 << 32)
+    return out.astype(dtype)
+
+
 def normal_array(seed: int, stream: int, shape, dtype=np.float32, offset: int = 0,
-                 chunk: int = 1 << 22):
-    """A whole array of the given shape; element i has flat index offset + i."""
+                 chunk: int = 1 << 22, full: bool = False):
+    """A whole array of the given shape; element i has flat index offset + i.  full=True takes
+    the full-mantissa variant."""
+    fn = full_values if full else normal_values
     n = int(np.prod(shape, dtype=np.int64))
     out = np.empty(n, dtype=dtype)
     for a in range(0, n, chunk):
         b = min(n, a + chunk)
-        out[a:b] = normal_values(seed, stream, np.arange(offset + a, offset + b, dtype=np.int64), dtype)
+        out[a:b] = fn(seed, stream, np.arange(offset + a, offset + b, dtype=np.int64), dtype)
     return out.reshape(shape)
 
 
@@ -103,17 +132,41 @@ def _byte_sum_t(w):
     return (t & 0xFFFF) + (t >> 16)
 
 
-def normal_values_torch(seed: int, stream: int, out, offset: int = 0, chunk: int = 1 << 28):
+def values_at_torch(seed: int, stream: int, idx, full: bool = False):
+    """The values at the flat indices `idx` (an int64 torch tensor on any device) as an exact
+    float64 tensor: normal_values() (full=True: full_values()) computed with torch ops, which
+    is faster on the host than NumPy for large index sets."""
+    import torch
+
+    lo = idx & M32
+    hi = idx >> 32
+    s = torch.zeros_like(idx)
+    for r in range(3):
+        k = key_for(seed, stream, r)
+        w = _mix32_t(_mix32_t(lo ^ k) ^ ((hi * _C3 + k) & M32))
+        s += _byte_sum_t(w)
+    if not full:
+        return (s - 1530).to(torch.float64) / 256.0
+    k = key_for(seed, stream, 3)
+    u = _mix32_t(_mix32_t(lo ^ k) ^ ((hi * _C3 + k) & M32)) >> 8
+    return ((s - 1530) * (1 << 24) + (u - (1 << 23))).to(torch.float64) / float(1 << 32)
+
+
+def normal_values_torch(seed: int, stream: int, out, offset: int = 0, chunk: int = 1 << 28,
+                        full: bool = False):
     """Fill the contiguous torch tensor `out` (any float dtype, any device) in place.
 
     Element i of `out.view(-1)` receives the value for flat index offset + i, the
-    same number normal_values() gives on the host.
+    same number normal_values() (full=True: full_values()) gives on the host.
     """
     import torch
 
     flat = out.view(-1)
     n = flat.numel()
     keys = [key_for(seed, stream, r) for r in range(3)]
+    k3 = key_for(seed, stream, 3)
+    if full:
+        chunk = min(chunk, 1 << 26)
     for a in range(0, n, chunk):
         b = min(n, a + chunk)
         idx = torch.arange(offset + a, offset + b, dtype=torch.int64, device=flat.device)
@@ -123,7 +176,13 @@ def normal_values_torch(seed: int, stream: int, out, offset: int = 0, chunk: int
         for k in keys:
             w = _mix32_t(_mix32_t(lo ^ k) ^ ((hi * _C3 + k) & M32))
             s += _byte_sum_t(w)
-        del idx, lo, hi
-        flat[a:b] = ((s - 1530).to(torch.float32) / 256.0).to(flat.dtype)
-        del s
+        if full:
+            u = _mix32_t(_mix32_t(lo ^ k3) ^ ((hi * _C3 + k3) & M32)) >> 8
+            num = (s - 1530) * (1 << 24) + (u - (1 << 23))
+            del u
+            flat[a:b] = (num.to(torch.float64) / float(1 << 32)).to(flat.dtype)
+            del num
+        else:
+            flat[a:b] = ((s - 1530).to(torch.float32) / 256.0).to(flat.dtype)
+        del idx, lo, hi, s
     return out
