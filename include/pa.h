@@ -203,6 +203,36 @@ int pa_decode_ext(void* out, const void* q,
                   void* stream);
 
 /*
+ * pa_decode_noalloc — pa_decode_ext for callers that cannot allocate: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, checks and results as pa_decode_ext, without
+ * the workspace: the partial results live in a device array inside the library
+ * (PA_NOALLOC_WORKSPACE_BYTES per device that loads it, held until the process
+ * ends).  The call allocates nothing and launches the same kernels.
+ *   A batch whose pa_decode_workspace_bytes(...) exceeds
+ *   PA_NOALLOC_WORKSPACE_BYTES returns PA_ERR_WORKSPACE and launches nothing
+ *   (for example 256 sequences x 40 heads x head_dim 128 fit up to contexts of
+ *   about 12,800 tokens; chunk query rows count as rows).
+ *   The first call on a device looks up that device's array address (a HIP
+ *   runtime query, with the stream's device made current for it and the
+ *   caller's current device restored); a failed lookup returns PA_ERR_LAUNCH.
+ *   Every call on one device shares its array: calls that may overlap in time
+ *   on one device (several streams or threads) race and must be serialised by
+ *   the caller.  The array needs no clearing between calls.
+ */
+#define PA_NOALLOC_WORKSPACE_BYTES ((size_t)256 << 20)
+
+int pa_decode_noalloc(void* out, const void* q,
+                      const void* k_pool, const void* v_pool, int64_t num_blocks,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, const int32_t* q_start_loc,
+                      int32_t num_seqs, int32_t num_tokens,
+                      int32_t max_context_len, int32_t max_query_len,
+                      int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t dtype,
+                      int32_t sliding_window, const float* alibi_slopes, uint32_t flags,
+                      void* stream);
+
+/*
  * pa_copy_blocks — copy-on-write block copies, batched: for every pair
  * (src, dst) of block_pairs (int32 [num_pairs][2], device), the whole block
  * k_pool[dst] = k_pool[src] and v_pool[dst] = v_pool[src], every slot filled

@@ -17,6 +17,7 @@ PA_SWAP_OUT, PA_SWAP_IN = 0, 1
 PA_DECODE_SHARED_BLOCKS = 1
 PA_DECODE_GROUP_SHIFT = 8  # group size g of the grouped decode in flag bits 8..11
 PA_CHECK_OK = 0xFFFFFFFFFFFFFFFF
+PA_NOALLOC_WORKSPACE_BYTES = 256 << 20  # the device array behind pa_decode_noalloc
 # pa_check_kind values
 CHECK_KINDS = {1: "START_LOC", 2: "QUERY_COUNT", 3: "CONTEXT_LEN", 4: "BLOCK_ID",
                5: "SLOT_REUSED", 6: "PAIR_ID", 7: "DEST_REUSED", 8: "DEST_IS_SOURCE"}
@@ -34,6 +35,9 @@ SIGNATURES = {
     "pa_decode_ext": (_c_int, [_vp, _vp, _vp, _vp, _c_i64, _vp, _c_i32, _vp, _vp, _c_i32, _c_i32,
                                _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _c_size, _c_i32,
                                _vp, ctypes.c_uint32, _vp]),
+    "pa_decode_noalloc": (_c_int, [_vp, _vp, _vp, _vp, _c_i64, _vp, _c_i32, _vp, _vp, _c_i32,
+                                   _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                   _vp, ctypes.c_uint32, _vp]),
     "pa_copy_blocks": (_c_int, [_vp, _vp, _c_i64, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                 _vp]),
     "pa_swap_blocks": (_c_int, [_vp, _vp, _c_i64, _vp, _vp, _c_i64, _vp, _c_i32, _c_i32, _c_i32,

@@ -287,5 +287,39 @@ def pa_decode_ext(out, q, k_pool, v_pool, block_tables, context_lens, q_start_lo
     return out
 
 
+def pa_decode_noalloc(out, q, k_pool, v_pool, block_tables, context_lens, q_start_loc=None,
+                      max_context_len: Optional[int] = None, max_query_len: int = 1,
+                      sliding_window: int = 0, alibi_slopes: Optional[torch.Tensor] = None,
+                      shared_blocks: bool = False, stream=None, group: int = 0) -> torch.Tensor:
+    """pa_decode_ext without a workspace argument: the partial results live in the library's
+    fixed device array (PA_NOALLOC_WORKSPACE_BYTES per device), so neither the library nor this
+    wrapper allocates.  Calls that overlap on one device race on that array.
+    max_context_len must be given (reading it from the device would synchronise)."""
+    nb, bs, h, d, dt = _check_pool(k_pool, v_pool)
+    S = context_lens.shape[0]
+    T = q.shape[0]
+    _check_index(block_tables, "block_tables", S)
+    _check_index(context_lens, "context_lens")
+    _check_index(q_start_loc, "q_start_loc", S + 1)
+    _require(q.shape == (T, h, d) and out.shape == q.shape, "q / out must be [T][H][d]")
+    _require(q.dtype == out.dtype == k_pool.dtype, "q / out dtype must match the pool")
+    _require(q.is_contiguous() and out.is_contiguous(), "q / out must be contiguous")
+    _require(0 <= int(group) <= 15, "group must be in 0..15 (2..6 are built)")
+    _require(max_context_len is not None, "max_context_len is required")
+    if alibi_slopes is not None:
+        _require(alibi_slopes.dtype == torch.float32 and alibi_slopes.is_cuda and
+                 alibi_slopes.is_contiguous() and alibi_slopes.numel() == h,
+                 "alibi_slopes must be a contiguous float32 GPU tensor [num_heads]")
+    st = _lib.load().pa_decode_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), nb, _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), _ptr(q_start_loc), S, T, int(max_context_len),
+        int(max_query_len), h, d, bs, dt, int(sliding_window), _ptr(alibi_slopes),
+        (_lib.PA_DECODE_SHARED_BLOCKS if shared_blocks else 0) |
+        (int(group) << _lib.PA_DECODE_GROUP_SHIFT),
+        _stream(stream))
+    _lib.check(st, "pa_decode_noalloc")
+    return out
+
+
 def pa_strerror(status: int) -> str:
     return _lib.strerror(status)

@@ -49,6 +49,94 @@ void* mapped_host_range(void* p, int64_t bytes) {
 
 }  // namespace
 
+namespace pa {
+
+int check_decode(const DecodeCall& c) {
+  if (int st = check_layout(c.num_blocks, c.num_heads, c.head_dim, c.block_size, c.dtype))
+    return st;
+  if (c.sliding_window < 0) return PA_ERR_SHAPE;
+  const uint32_t group_bits = 0xFu << PA_DECODE_GROUP_SHIFT;
+  if (c.flags & ~(static_cast<uint32_t>(PA_DECODE_SHARED_BLOCKS) | group_bits))
+    return PA_ERR_UNSUPPORTED;
+  const int group = static_cast<int>((c.flags & group_bits) >> PA_DECODE_GROUP_SHIFT);
+  if (group > 1 && (group > kMaxDecodeGroup || (c.flags & PA_DECODE_SHARED_BLOCKS) ||
+                    c.dtype != PA_F16 || c.q_start_loc != nullptr || c.sliding_window != 0))
+    return PA_ERR_UNSUPPORTED;
+  if (c.num_seqs <= 0 || c.num_tokens <= 0 || c.max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  if (c.max_context_len <= 0 || c.max_query_len <= 0 || c.max_query_len > c.max_context_len)
+    return PA_ERR_SHAPE;
+  if (static_cast<int64_t>(c.max_context_len) >
+      static_cast<int64_t>(c.max_blocks_per_seq) * c.block_size)
+    return PA_ERR_SHAPE;
+  if (c.q_start_loc == nullptr && (c.num_tokens != c.num_seqs || c.max_query_len != 1))
+    return PA_ERR_SHAPE;
+  // grid limits of the decode launch: z = sequences, y = context partitions
+  if (c.num_seqs > 65535 || c.max_context_len / kMinPartition >= 65535) return PA_ERR_SHAPE;
+  // shared-block mode launches one-dimensionally: (head groups x sequences x partitions)
+  // workgroups of 256 work-items must stay below 2^32 work-items
+  if ((c.flags & PA_DECODE_SHARED_BLOCKS) &&
+      static_cast<int64_t>(c.num_heads) * c.num_seqs *
+              ((c.max_context_len + kMinPartition - 1) / kMinPartition) >= (int64_t{1} << 24))
+    return PA_ERR_SHAPE;
+  if (!c.out || !c.q || !c.k_pool || !c.v_pool || !c.block_tables || !c.context_lens)
+    return PA_ERR_NULL;
+  // the multi-query tile path is built for fp16 (head_dim 64 or 128, as everywhere)
+  if (c.max_query_len > 1 && c.dtype != PA_F16) return PA_ERR_UNSUPPORTED;
+  if (c.max_query_len > 1 && (c.max_query_len + 63) / 64 > 65535) return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+int run_decode(const DecodeCall& c, void* workspace, hipStream_t st) {
+  const uint32_t group_bits = 0xFu << PA_DECODE_GROUP_SHIFT;
+  const int group = static_cast<int>((c.flags & group_bits) >> PA_DECODE_GROUP_SHIFT);
+  DecodeArgs a{};
+  a.out = c.out;
+  a.q = c.q;
+  a.k_pool = c.k_pool;
+  a.v_pool = c.v_pool;
+  a.num_blocks = c.num_blocks;
+  a.block_tables = c.block_tables;
+  a.max_blocks = c.max_blocks_per_seq;
+  a.context_lens = c.context_lens;
+  a.q_start_loc = c.q_start_loc;
+  a.num_seqs = c.num_seqs;
+  a.num_tokens = c.num_tokens;
+  a.num_heads = c.num_heads;
+  a.block_size = c.block_size;
+  a.max_context_len = c.max_context_len;
+  a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(c.head_dim)));
+  a.window = c.sliding_window;
+  a.alibi = c.alibi_slopes;
+  a.flags = c.flags & PA_DECODE_SHARED_BLOCKS;
+  a.group = group > 1 ? group : 0;
+  a.workspace = workspace;
+  // single-query sequences: context partitions + merge; the kernels skip the others
+  int status = launch_status(
+      launch_decode(a, c.dtype, c.head_dim, c.block_size, c.max_context_len, st));
+  if (status != PA_OK || c.max_query_len <= 1) return status;
+  // sequences with several queries: causal MFMA tiles
+  TileArgs ta{};
+  ta.out = c.out;
+  ta.q = c.q;
+  ta.k_pool = c.k_pool;
+  ta.v_pool = c.v_pool;
+  ta.num_blocks = c.num_blocks;
+  ta.block_tables = c.block_tables;
+  ta.max_blocks = c.max_blocks_per_seq;
+  ta.context_lens = c.context_lens;
+  ta.q_start_loc = c.q_start_loc;
+  ta.num_seqs = c.num_seqs;
+  ta.num_tokens = c.num_tokens;
+  ta.num_heads = c.num_heads;
+  ta.scale_log2 = a.scale_log2;
+  ta.window = c.sliding_window;
+  ta.alibi = c.alibi_slopes;
+  return launch_status(launch_tile(ta, workspace, c.head_dim, c.block_size, c.max_query_len,
+                                   c.max_context_len, st));
+}
+
+}  // namespace pa
+
 extern "C" {
 
 const char* pa_strerror(int status) {
@@ -145,82 +233,14 @@ int pa_decode_ext(void* out, const void* q, const void* k_pool, const void* v_po
                   int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t dtype,
                   void* workspace, size_t workspace_bytes, int32_t sliding_window,
                   const float* alibi_slopes, uint32_t flags, void* stream) {
-  if (int st = check_layout(num_blocks, num_heads, head_dim, block_size, dtype)) return st;
-  if (sliding_window < 0) return PA_ERR_SHAPE;
-  const uint32_t group_bits = 0xFu << PA_DECODE_GROUP_SHIFT;
-  if (flags & ~(static_cast<uint32_t>(PA_DECODE_SHARED_BLOCKS) | group_bits))
-    return PA_ERR_UNSUPPORTED;
-  const int group = static_cast<int>((flags & group_bits) >> PA_DECODE_GROUP_SHIFT);
-  if (group > 1 && (group > pa::kMaxDecodeGroup || (flags & PA_DECODE_SHARED_BLOCKS) ||
-                    dtype != PA_F16 || q_start_loc != nullptr || sliding_window != 0))
-    return PA_ERR_UNSUPPORTED;
-  if (num_seqs <= 0 || num_tokens <= 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
-  if (max_context_len <= 0 || max_query_len <= 0 || max_query_len > max_context_len)
-    return PA_ERR_SHAPE;
-  if (static_cast<int64_t>(max_context_len) >
-      static_cast<int64_t>(max_blocks_per_seq) * block_size)
-    return PA_ERR_SHAPE;
-  if (q_start_loc == nullptr && (num_tokens != num_seqs || max_query_len != 1))
-    return PA_ERR_SHAPE;
-  // grid limits of the decode launch: z = sequences, y = context partitions
-  if (num_seqs > 65535 || max_context_len / pa::kMinPartition >= 65535) return PA_ERR_SHAPE;
-  // shared-block mode launches one-dimensionally: (head groups x sequences x partitions)
-  // workgroups of 256 work-items must stay below 2^32 work-items
-  if ((flags & PA_DECODE_SHARED_BLOCKS) &&
-      static_cast<int64_t>(num_heads) * num_seqs *
-              ((max_context_len + pa::kMinPartition - 1) / pa::kMinPartition) >= (int64_t{1} << 24))
-    return PA_ERR_SHAPE;
-  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PA_ERR_NULL;
-  // the multi-query tile path is built for fp16 (head_dim 64 or 128, as everywhere)
-  if (max_query_len > 1 && dtype != PA_F16) return PA_ERR_UNSUPPORTED;
-  if (max_query_len > 1 && (max_query_len + 63) / 64 > 65535) return PA_ERR_SHAPE;
+  pa::DecodeCall c{out, q, k_pool, v_pool, num_blocks, block_tables, max_blocks_per_seq,
+                   context_lens, q_start_loc, num_seqs, num_tokens, max_context_len,
+                   max_query_len, num_heads, head_dim, block_size, dtype, sliding_window,
+                   alibi_slopes, flags};
+  if (int st = pa::check_decode(c)) return st;
   const size_t need = pa::decode_workspace_bytes(num_tokens, num_heads, head_dim, max_context_len);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_WORKSPACE;
-
-  pa::DecodeArgs a{};
-  a.out = out;
-  a.q = q;
-  a.k_pool = k_pool;
-  a.v_pool = v_pool;
-  a.num_blocks = num_blocks;
-  a.block_tables = block_tables;
-  a.max_blocks = max_blocks_per_seq;
-  a.context_lens = context_lens;
-  a.q_start_loc = q_start_loc;
-  a.num_seqs = num_seqs;
-  a.num_tokens = num_tokens;
-  a.num_heads = num_heads;
-  a.block_size = block_size;
-  a.max_context_len = max_context_len;
-  a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(head_dim)));
-  a.window = sliding_window;
-  a.alibi = alibi_slopes;
-  a.flags = flags & PA_DECODE_SHARED_BLOCKS;
-  a.group = group > 1 ? group : 0;
-  a.workspace = workspace;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  // single-query sequences: context partitions + merge; the kernels skip the others
-  int status = launch_status(pa::launch_decode(a, dtype, head_dim, block_size, max_context_len, st));
-  if (status != PA_OK || max_query_len <= 1) return status;
-  // sequences with several queries: causal MFMA tiles
-  pa::TileArgs ta{};
-  ta.out = out;
-  ta.q = q;
-  ta.k_pool = k_pool;
-  ta.v_pool = v_pool;
-  ta.num_blocks = num_blocks;
-  ta.block_tables = block_tables;
-  ta.max_blocks = max_blocks_per_seq;
-  ta.context_lens = context_lens;
-  ta.q_start_loc = q_start_loc;
-  ta.num_seqs = num_seqs;
-  ta.num_tokens = num_tokens;
-  ta.num_heads = num_heads;
-  ta.scale_log2 = a.scale_log2;
-  ta.window = sliding_window;
-  ta.alibi = alibi_slopes;
-  return launch_status(
-      pa::launch_tile(ta, workspace, head_dim, block_size, max_query_len, max_context_len, st));
+  return pa::run_decode(c, workspace, static_cast<hipStream_t>(stream));
 }
 
 size_t pa_check_workspace_bytes(int64_t num_marks) {

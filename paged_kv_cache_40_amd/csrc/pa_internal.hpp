@@ -66,6 +66,37 @@ struct TileArgs {
   float* ws_ml;            // [num_tokens][num_heads][num_parts_max][2] = (max, sum), log2 domain
 };
 
+// The arguments of one attention call (pa_decode_ext without its workspace), as the C ABI
+// received them.
+struct DecodeCall {
+  void* out;
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  int64_t num_blocks;
+  const int32_t* block_tables;
+  int32_t max_blocks_per_seq;
+  const int32_t* context_lens;
+  const int32_t* q_start_loc;
+  int32_t num_seqs;
+  int32_t num_tokens;
+  int32_t max_context_len;
+  int32_t max_query_len;
+  int32_t num_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t dtype;
+  int32_t sliding_window;
+  const float* alibi_slopes;
+  uint32_t flags;
+};
+
+// Host-side argument checks of an attention call (everything but the workspace): PA_OK or the
+// pa_status of the first failure.  No HIP call.
+int check_decode(const DecodeCall& c);
+// Launch the checked call with a workspace of at least decode_workspace_bytes(...) bytes.
+int run_decode(const DecodeCall& c, void* workspace, hipStream_t stream);
+
 // Largest sequence group of the grouped decode (fp16, no window, one query per
 // sequence).
 constexpr int kMaxDecodeGroup = 6;

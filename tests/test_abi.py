@@ -237,3 +237,30 @@ def check_pairs(lib, **kw):
 ])
 def test_check_pairs_rejects(lib, kw, code):
     assert check_pairs(lib, **kw) == code
+
+
+def noalloc(lib, **kw):
+    a = dict(o=FAKE, q=FAKE, k=FAKE, v=FAKE, nb=64, bt=FAKE, mb=8, cl=FAKE, qsl=None, S=4, T=4,
+             mcl=100, mql=1, H=2, D=64, B=16, dt=0, W=0, al=None, fl=0)
+    a.update(kw)
+    return lib.pa_decode_noalloc(a["o"], a["q"], a["k"], a["v"], a["nb"], a["bt"], a["mb"],
+                                 a["cl"], a["qsl"], a["S"], a["T"], a["mcl"], a["mql"], a["H"],
+                                 a["D"], a["B"], a["dt"], a["W"], a["al"], a["fl"], None)
+
+
+def test_noalloc_rejects_before_any_hip_call(lib):
+    from paged_kv_cache_40_amd import _lib
+    # the same host checks as pa_decode_ext
+    assert noalloc(lib, o=None) == -1
+    assert noalloc(lib, D=96) == -3
+    assert noalloc(lib, mcl=200, mb=8) == -2          # context past the table width
+    assert noalloc(lib, fl=1 << 31) == -3
+    # a batch whose partials exceed the library's array: PA_ERR_WORKSPACE, nothing launched
+    S, H, D, L = 256, 40, 128, 16384
+    need = lib.pa_decode_workspace_bytes(S, H, D, L)
+    assert need > _lib.PA_NOALLOC_WORKSPACE_BYTES
+    assert noalloc(lib, S=S, T=S, H=H, D=D, mcl=L, mb=L // 16, nb=1 << 20, dt=1) == -4
+    # the largest such decode batch that fits: about 12,800 tokens for 256 x 40 heads
+    fits = max(L for L in range(256, 20000, 256)
+               if lib.pa_decode_workspace_bytes(S, H, D, L) <= _lib.PA_NOALLOC_WORKSPACE_BYTES)
+    assert 12000 <= fits <= 13000
