@@ -93,6 +93,20 @@ def hbm_stream_read_gbs(buf, reps: int = 5) -> float:
 
 # ---------------------------------------------------------------- cpu leg --
 
+# Oracle worker processes: every core the process may run on, at most 16 - one GPU's share of
+# the host cores where this runs (os.cpu_count() reports the whole machine).  The record
+# carries host_cores, available_cores and the workers actually used.
+CPU_WORKER_CAP = 16
+
+
+def default_cpu_workers() -> int:
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return max(1, min(CPU_WORKER_CAP, avail))
+
+
 def _cpu_worker(args):
     shm, i = args
     import numpy as np
@@ -148,8 +162,14 @@ def cpu_baseline(w, t, nseq: int, workers: int):
             os.unlink(os.path.join(shm, f))
         os.rmdir(shm)
     kv = 2 * int(w.context_lens[seqs].astype(np.int64).sum()) * w.num_heads * w.head_dim * w.elt_bytes
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
     return {
         "value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": workers, "kind": "oracle",
+        "host_cores": os.cpu_count(), "available_cores": avail, "workers": workers,
+        "worker_cap": CPU_WORKER_CAP,
         "seconds": round(dt, 3),
         "seq_heads_per_s": round(len(seqs) * w.num_heads / dt, 1),
         "sample": f"first {len(seqs)} of {w.num_seqs} sequences (all {w.num_heads} heads): the "
@@ -740,7 +760,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=5)
     ap.add_argument("--cpu-seqs", type=int, default=256, help="oracle sample size (0 = skip)")
-    ap.add_argument("--cpu-workers", type=int, default=0, help="0 = min(16, host cores)")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="0 = every core this process may run on, at most CPU_WORKER_CAP")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (PMC byte calibration)")
     ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5],
@@ -809,7 +830,7 @@ def main(argv=None) -> int:
 
     cpu = None
     if args.cpu_seqs > 0:
-        workers = args.cpu_workers or min(16, os.cpu_count() or 1)
+        workers = args.cpu_workers or default_cpu_workers()
         print(f"[bench] cpu baseline: {args.cpu_seqs} sequences on {workers} workers",
               file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, t, args.cpu_seqs, workers)

@@ -179,12 +179,10 @@ int pa_decode(void* out, const void* q,
  *   rounding, not bit for bit.  Built for dtype PA_F16 with q_start_loc NULL
  *   and sliding_window 0 (ALiBi slopes allowed), and not combined with
  *   PA_DECODE_SHARED_BLOCKS: other uses return PA_ERR_UNSUPPORTED.  g = 0 or 1
- *   means no runs.  Choosing between the two: the grouped decode gives each run's
- *   shared rows to one wave, so it needs enough runs to fill the GPU; when
- *   ceil(num_seqs / g) * num_heads * ceil(max_context_len / 256) is below about
- *   1,536 the shared-blocks hint is faster (measured on MI355X: 16 runs of 6
- *   samples x 5 heads, 0.083 vs 0.107 ms per decode step; x 40 heads, 0.338 vs
- *   0.267 ms in favour of the runs).
+ *   means no runs.  Choosing between the two: the grouped decode needs enough
+ *   runs x heads to fill the GPU; below about 1,536 units of
+ *   ceil(num_seqs / g) * num_heads * ceil(max_context_len / 256) the
+ *   shared-blocks hint is usually faster.
  * pa_decode(...) is pa_decode_ext(..., 0, NULL, 0, stream).  Both variants
  * apply to every query row, single-query decodes and multi-query chunks alike
  * (a chunk's query at position p sees its own window p-W+1 .. p).

@@ -48,51 +48,18 @@
 #include "pa_common.hpp"
 #include "pa_internal.hpp"
 
-// Build-time tuning knobs (defaults are the measured best on MI355X).
-#ifndef PA_DECODE_PARTITION
-#define PA_DECODE_PARTITION 0  // 0: chosen per launch (see pick_partition); else forced
-#endif
-#ifndef PA_DECODE_TRIP_U
-#define PA_DECODE_TRIP_U 0  // iterations per trip (0: one)
-#endif
-#ifndef PA_DECODE_NT_LOADS
-#define PA_DECODE_NT_LOADS 1  // K/V are read once: streaming (non-temporal) loads
-#endif
-#ifndef PA_DECODE_HEADS_PER_WG
-#define PA_DECODE_HEADS_PER_WG 4  // waves per workgroup (one head each) when it divides the heads
-#endif
-#ifndef PA_DECODE_BALANCED
-#define PA_DECODE_BALANCED 1  // 1: a sequence's partitions share its tokens evenly
-#endif
-#ifndef PA_DECODE_GRID_ORDER
-#define PA_DECODE_GRID_ORDER 2  // 2: head group fastest, then sequence, then partition
-#endif
-#ifndef PA_DECODE_WAVES_PER_EU
-#define PA_DECODE_WAVES_PER_EU 0  // 0: compiler's choice; n: ask for n waves per SIMD
-#endif
-#if PA_DECODE_WAVES_PER_EU > 0
-#define PA_DECODE_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES_PER_EU)))
-#else
-#define PA_DECODE_OCCUPANCY
-#endif
-
 namespace pa {
-
-static_assert(PA_DECODE_PARTITION == 0 || PA_DECODE_PARTITION >= kMinPartition,
-              "partition below the workspace sizing");
 
 // K/V loads.  Unshared batches stream (each row is read once: the non-temporal hint keeps it
 // from displacing useful lines); batches whose neighbouring sequences share blocks keep the
 // rows cached so the sharers find them in L2.
 template <bool kShared>
 __device__ __forceinline__ u32x4 ld_kv(const void* p) {
-#if PA_DECODE_NT_LOADS
   if constexpr (!kShared) return ld16_stream(p);
-#endif
   return ld16(p);
 }
 
-template <typename T, int D, int BS, int P, int kTripU = PA_DECODE_TRIP_U>
+template <typename T, int D, int BS, int P, int kTripU = 1>
 struct DecodeCfg {
   static constexpr int kElt = sizeof(T);
   static constexpr int kRow = D * kElt;        // bytes of one head's row of one token
@@ -101,7 +68,7 @@ struct DecodeCfg {
   static constexpr int kTpi = 8 * kR;          // tokens per iteration
   static constexpr int kEpc = 16 / kElt;       // elements per 16-byte chunk
   static constexpr int kEpl = kCpt * kEpc;     // elements (head dims) per lane
-  static constexpr int kU = kTripU > 0 ? kTripU : 1;  // iterations per trip
+  static constexpr int kU = kTripU;             // iterations per trip
   static constexpr int kG = kU * kR;           // token groups per lane per trip
   static constexpr int kTrip = kU * kTpi;      // tokens per trip
   static constexpr int kBlocks = P / BS;       // table entries per partition
@@ -119,25 +86,13 @@ constexpr float kTau = 8.0f;  // log2 headroom before the running reference move
 // one.  A partial last group would leave wave slots empty in every (sequence, partition):
 // 5 heads in groups of 4 fill 5 of 8 slots, and one head per workgroup runs such batches
 // 1.3-1.6x faster, while with 40 heads groups of 4 beat single heads by 4%.
-constexpr int kHeadsPerWg = PA_DECODE_HEADS_PER_WG;
-constexpr int kXcds = 8;  // accelerator complex dies of an MI355X
-#ifndef PA_DECODE_XCD_CHUNK
-#define PA_DECODE_XCD_CHUNK 128  // work units per run on one XCD (shared-block mode)
-#endif
-constexpr int kXcdChunk = PA_DECODE_XCD_CHUNK;
-#ifndef PA_DECODE_GROUP_TRIP_U
-#define PA_DECODE_GROUP_TRIP_U 0  // grouped decode: iterations per trip (0: by run capacity)
-#endif
-#ifndef PA_DECODE_GROUP_REST_DIV
-#define PA_DECODE_GROUP_REST_DIV 8  // grouped decode: joint only if no member adds > P/this
-#endif
-#ifndef PA_DECODE_GROUP_PARTITION
-#define PA_DECODE_GROUP_PARTITION 0  // grouped decode: 0 = default (512), else 256/512/1024
-#endif
+constexpr int kHeadsPerWg = 4;
+constexpr int kXcds = 8;        // accelerator complex dies of an MI355X
+constexpr int kXcdChunk = 128;  // work units per run on one XCD (shared-block mode)
+constexpr int kGroupRestDiv = 8;  // grouped decode: joint only if no member adds > P/8 tokens
 
 template <typename T, int D, int BS, int P, bool kShared>
-__global__ __launch_bounds__(64 * kHeadsPerWg) PA_DECODE_OCCUPANCY
-void decode_partition_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kHeadsPerWg) void decode_partition_kernel(DecodeArgs a) {
   using C = DecodeCfg<T, D, BS, P>;
   int hg, s, part;
   if constexpr (kShared) {
@@ -161,13 +116,8 @@ void decode_partition_kernel(DecodeArgs a) {
     hg = (n / a.num_seqs) % hgroups;
     part = n / (hgroups * a.num_seqs);
   } else {
-#if PA_DECODE_GRID_ORDER == 1
-    part = blockIdx.x, hg = blockIdx.y, s = blockIdx.z;
-#elif PA_DECODE_GRID_ORDER == 2
+    // head group fastest, then sequence, then partition
     hg = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
-#else
-    hg = blockIdx.x, part = blockIdx.y, s = blockIdx.z;
-#endif
   }
   const int h = hg * a.heads_per_wg + static_cast<int>(threadIdx.x >> 6);
   if (h >= a.num_heads) return;
@@ -190,12 +140,8 @@ void decode_partition_kernel(DecodeArgs a) {
   const int first = lo / BS * BS;
   const int span = ctx - first;
   const int nparts = (span + P - 1) / P;
-#if PA_DECODE_BALANCED
   // equal shares (rounded up to whole trips and blocks), so no partition is a short tail
   const int share = ((span + nparts - 1) / nparts + C::kAlign - 1) / C::kAlign * C::kAlign;
-#else
-  const int share = P;
-#endif
   const int start = first + part * share;
   if (start >= ctx) {
     // Rounded-up shares can leave a trailing partition without tokens; the merge pass
@@ -457,12 +403,11 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
 // grouping only says where sharing is likely.  Partials use the plain kernel's workspace
 // slots and merge pass.
 template <int D, int BS, int P, int kCap, bool kAlibi>
-__global__ __launch_bounds__(64 * kHeadsPerWg) PA_DECODE_OCCUPANCY
-void decode_group_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kHeadsPerWg) void decode_group_kernel(DecodeArgs a) {
   using T = f16;
-  using C = DecodeCfg<T, D, BS, P, (PA_DECODE_GROUP_TRIP_U > 0 ? PA_DECODE_GROUP_TRIP_U : 1)>;
-  constexpr int kRest = P / PA_DECODE_GROUP_REST_DIV;  // most tokens one member may add past
-                                                       // the shared prefix
+  using C = DecodeCfg<T, D, BS, P>;
+  constexpr int kRest = P / kGroupRestDiv;  // most tokens one member may add past the shared
+                                            // prefix
   const int hg = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
   const int h = hg * a.heads_per_wg + static_cast<int>(threadIdx.x >> 6);
   if (h >= a.num_heads) return;
@@ -817,13 +762,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a0, int max_context_len, hip
     hipLaunchKernelGGL((decode_partition_kernel<T, D, BS, P, true>), grid1, block1, 0, stream,
                        a);
   } else {
-#if PA_DECODE_GRID_ORDER == 1
-    dim3 grid1(nparts, hgroups, a.num_seqs);
-#elif PA_DECODE_GRID_ORDER == 2
     dim3 grid1(hgroups, a.num_seqs, nparts);
-#else
-    dim3 grid1(hgroups, nparts, a.num_seqs);
-#endif
     hipLaunchKernelGGL((decode_partition_kernel<T, D, BS, P, false>), grid1, block1, 0, stream,
                        a);
   }
@@ -840,7 +779,6 @@ static hipError_t launch_decode_t(const DecodeArgs& a0, int max_context_len, hip
 constexpr int64_t kTargetWaves = 16384;
 
 static int pick_partition(const DecodeArgs& a, int block_size, int max_context_len) {
-  if (PA_DECODE_PARTITION > 0) return PA_DECODE_PARTITION;
   const int cap = block_size == 8 ? 1024 : 2048;
   const int64_t units = static_cast<int64_t>(a.num_seqs) * a.num_heads;
   int p = cap;
@@ -911,7 +849,6 @@ static hipError_t launch_group_cap(const DecodeArgs& a, int max_context_len, hip
 constexpr int64_t kGroupTargetWaves = 1536;
 
 static int pick_group_partition(const DecodeArgs& a, int max_context_len) {
-  if (PA_DECODE_GROUP_PARTITION > 0) return PA_DECODE_GROUP_PARTITION;
   const int64_t units =
       static_cast<int64_t>((a.num_seqs + a.group - 1) / a.group) * a.num_heads;
   int p = 1024;

@@ -136,28 +136,15 @@ __device__ __forceinline__ int tile_splits(const TileArgs& a, int steps) {
 // chunk + decode batch at 32/16/8/4 heads, splitting pays only below it (4 heads: 94 vs
 // 134 us, 8 heads: 151 vs 167 us); at 16 heads (512 workgroups) splitting into 2 costs 25%
 // and at 32 heads into 2-4 costs 25-30% (partial writes, merge, re-staged keys).
-#ifndef PA_TILE_SPLIT_TARGET
-#define PA_TILE_SPLIT_TARGET 512
-#endif
-#ifndef PA_TILE_MIN_SPLIT_STEPS
-#define PA_TILE_MIN_SPLIT_STEPS 16
-#endif
-constexpr int64_t kSplitTargetWgs = PA_TILE_SPLIT_TARGET;
-constexpr int kMinSplitSteps = PA_TILE_MIN_SPLIT_STEPS;
+constexpr int64_t kSplitTargetWgs = 512;
+constexpr int kMinSplitSteps = 16;
 
 }  // namespace
 
-#ifndef PA_TILE_WAVES_PER_EU
-#define PA_TILE_WAVES_PER_EU 2
-#endif
-#if PA_TILE_WAVES_PER_EU > 0
-#define PA_TILE_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_TILE_WAVES_PER_EU)))
-#else
-#define PA_TILE_OCCUPANCY
-#endif
-
+// two waves per SIMD: the register budget of 32 queries per wave
 template <int D, int BS, bool kWindow, bool kAlibi, bool kSplit>
-__global__ __launch_bounds__(256) PA_TILE_OCCUPANCY void tile_attention_kernel(TileArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void tile_attention_kernel(TileArgs a) {
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
   using G = TileGeom<D>;
   constexpr int kD = D;
