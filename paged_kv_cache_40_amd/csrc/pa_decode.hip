@@ -89,7 +89,6 @@ constexpr float kTau = 8.0f;  // log2 headroom before the running reference move
 constexpr int kHeadsPerWg = 4;
 constexpr int kXcds = 8;        // accelerator complex dies of an MI355X
 constexpr int kXcdChunk = 128;  // work units per run on one XCD (shared-block mode)
-constexpr int kGroupRestDiv = 8;  // grouped decode: joint only if no member adds > P/8 tokens
 
 template <typename T, int D, int BS, int P, bool kShared>
 __global__ __launch_bounds__(64 * kHeadsPerWg) void decode_partition_kernel(DecodeArgs a) {
@@ -387,57 +386,63 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
 
 // Grouped decode [P1 sec. 6, parallel-sampling and beam-search paragraphs: the samples of
 // one prompt share its blocks, beam candidates share their common ancestry].  When the caller
-// places such
-// sequences next to each other, in runs of G, the shared rows need only be read once for
-// the whole run.  Partitions are fixed (tokens [p*P, (p+1)*P)), so the members' partitions
-// line up.  For each (run, partition) every wave of the run works out, from the members'
-// context lengths and table entries alone:
-//   t = the longest prefix of the partition, in whole trips, that every member's context
-//       covers and whose blocks are the same physical blocks for every member;
-// and the run is handled jointly when t > 0 and no member has more than kRest further
-// tokens in the partition.  Then the run's first wave reads the t tokens' K/V rows once,
-// updates every member's running (m, l, acc) from them, and afterwards takes each member's
-// remaining tokens on its own; the other members' waves exit.  Otherwise each wave reads
-// its own sequence's partition, as the plain kernel does.  Since all waves decide alike,
-// every (sequence, head, partition) is computed exactly once whatever the tables hold: the
-// grouping only says where sharing is likely.  Partials use the plain kernel's workspace
-// slots and merge pass.
+// places such sequences next to each other, in runs of G, their shared rows need only be read
+// once for the whole run.  One workgroup of kGroupWaves waves handles one (run, head,
+// partition of P tokens); partitions are fixed token ranges [p*P, (p+1)*P), so the members'
+// partitions line up.  From the members' context lengths and table entries alone it works out:
+//   * the active members: those whose context reaches into the partition;
+//   * t = the longest prefix of the partition, in whole trips, that every active member's
+//     context covers and whose blocks are the same physical blocks for all of them (at least
+//     two active members, else 0);
+//   * the work items: the t / kTrip joint trips (each token row read once, through the first
+//     active member's entries, and used for every active member), then each active member's
+//     own trips from t to the end of its context in the partition (its own entries).
+// The items are dealt to the waves round-robin, so the shared rows and the private tails are
+// spread over all waves of the workgroup, and each wave's loads run one item ahead of its
+// arithmetic (two register buffers).  Every wave keeps a running (m, l, acc) per member; at
+// the end the waves' states are merged per member in LDS with the online-softmax rule and the
+// member's partial (or, for a single-partition context, its output) is written.  Since the
+// split is a function of the tables alone, every (sequence, head, token) is used exactly once,
+// through a block equal to its own table entry, whatever the tables hold: a wrong grouping
+// costs speed, never correctness.  Partials use the plain kernel's workspace slots and merge.
+constexpr int kGroupWaves = 4;
+
 template <int D, int BS, int P, int kCap, bool kAlibi>
-__global__ __launch_bounds__(64 * kHeadsPerWg) void decode_group_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kGroupWaves) void decode_group_kernel(DecodeArgs a) {
   using T = f16;
   using C = DecodeCfg<T, D, BS, P>;
-  constexpr int kRest = P / kGroupRestDiv;  // most tokens one member may add past the shared
-                                            // prefix
-  const int hg = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
-  const int h = hg * a.heads_per_wg + static_cast<int>(threadIdx.x >> 6);
-  if (h >= a.num_heads) return;
+  const int h = blockIdx.x;
+  const int lead = static_cast<int>(blockIdx.y) * a.group;
+  const int part = blockIdx.z;
+  // the wave index, known to the compiler as wave-uniform: the item bookkeeping below then
+  // runs on the scalar unit
+  const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   const int g = lane >> 3;  // token within a group of 8
   const int c = lane & 7;   // 16-byte column within a 128-byte line
-
+  const int nmem = min(a.group, a.num_seqs - lead);
   const int cap = min(a.max_blocks * BS, a.max_context_len);
   const int start = part * P;
-  if (min(a.context_lens[s], cap) <= start) return;  // no tokens of this sequence here
-  const int lead = s - s % a.group;
-  const int nmem = min(a.group, a.num_seqs - lead);
 
-  // members' clamped context lengths and their table entries for this partition
-  int ctxk[kCap];
+  // members' clamped context lengths, their tokens in this partition (0: inactive) and their
+  // table entries for it; the same values in every thread of the workgroup
+  int ctxk[kCap], endk[kCap];
   int blk[kCap][C::kTabRegs];
-  bool all_in = nmem > 1;
-  int min_ctx = cap, max_ctx = 0;
+  int nact = 0, first = -1, reach = P;
 #pragma unroll
   for (int k = 0; k < kCap; ++k) {
     ctxk[k] = 0;
+    endk[k] = 0;
 #pragma unroll
     for (int r = 0; r < C::kTabRegs; ++r) blk[k][r] = 0;
     if (k < nmem) {
       ctxk[k] = min(a.context_lens[lead + k], cap);
-      all_in = all_in && ctxk[k] > start;
-      min_ctx = min(min_ctx, ctxk[k]);
-      max_ctx = max(max_ctx, ctxk[k]);
       if (ctxk[k] > start) {
-        const int nb = (min(ctxk[k] - start, P) + BS - 1) / BS;
+        endk[k] = min(ctxk[k] - start, P);
+        ++nact;
+        if (first < 0) first = k;
+        reach = min(reach, endk[k]);
+        const int nb = (endk[k] + BS - 1) / BS;
         const int32_t* bt =
             a.block_tables + static_cast<int64_t>(lead + k) * a.max_blocks + start / BS;
 #pragma unroll
@@ -450,72 +455,62 @@ __global__ __launch_bounds__(64 * kHeadsPerWg) void decode_group_kernel(DecodeAr
       }
     }
   }
+  if (nact == 0) return;  // the same in every thread: no member has tokens here
 
+  // entries of the first active member: the joint trips read through them
+  int fb[C::kTabRegs];
+#pragma unroll
+  for (int r = 0; r < C::kTabRegs; ++r) {
+    fb[r] = 0;
+#pragma unroll
+    for (int k = 0; k < kCap; ++k)
+      if (k == first) fb[r] = blk[k][r];
+  }
   int t = 0;  // shared prefix of the partition, in tokens (a multiple of the trip)
-  if (all_in) {
-    const int reach = min(min_ctx - start, P);  // tokens every member has in the partition
-    const int nchk = (reach + BS - 1) / BS;     // blocks holding them
+  if (nact >= 2) {
+    const int nchk = (reach + BS - 1) / BS;  // blocks holding the tokens every member has
     int first_diff = nchk;
 #pragma unroll
     for (int r = C::kTabRegs - 1; r >= 0; --r) {
       bool same = true;
 #pragma unroll
-      for (int k = 1; k < kCap; ++k)
-        if (k < nmem) same = same && blk[k][r] == blk[0][r];
+      for (int k = 0; k < kCap; ++k)
+        if (endk[k] > 0) same = same && blk[k][r] == fb[r];
       const uint64_t diff = __ballot(r * kWave + lane < nchk && !same);
       if (diff != 0) first_diff = r * kWave + __builtin_ctzll(diff);
     }
     t = min(first_diff * BS, reach) / C::kTrip * C::kTrip;
-    if (min(max_ctx - start, P) - t > kRest) t = 0;
   }
-  const bool joint = t > 0;
-  if (joint && s != lead) return;  // the run's first wave computes this partition for all
-  const int base_seq = joint ? lead : s;  // sequence of state slot 0
-  const int nact = joint ? nmem : 1;      // state slots in use
+  // work items: joint trips [0, nj), then member k's own trips [pstart[k], pstart[k + 1])
+  const int nj = t / C::kTrip;
+  int pstart[kCap + 1];
+  pstart[0] = nj;
+#pragma unroll
+  for (int k = 0; k < kCap; ++k)
+    pstart[k + 1] = pstart[k] + (endk[k] > 0 ? (endk[k] - t + C::kTrip - 1) / C::kTrip : 0);
+  const int total = pstart[kCap];
 
-  const int64_t row_stride = static_cast<int64_t>(a.num_heads) * D;
+  // the members' query chunks in LDS, one copy per lane slot (written by wave k % kGroupWaves,
+  // read by all after the barrier); after them the per-wave states for the final merge
+  extern __shared__ u32x4 smem[];
+  auto q_slot = [&](int k, int j) -> u32x4& { return smem[(k * C::kCpt + j) * kWave + lane]; };
   auto col = [&](int j) { return (j * 8 + c) * C::kEpc; };
-  const T* kbase = static_cast<const T*>(a.k_pool) + static_cast<int64_t>(h) * D;
-  const T* vbase = static_cast<const T*>(a.v_pool) + static_cast<int64_t>(h) * D;
-
-  // the members' query chunks live in LDS, one private copy per lane (no lane reads another's
-  // slot, so no barrier is needed); the registers they free hold the next trip's loads
-  extern __shared__ u32x4 q_lds[];  // [heads_per_wg][kCap][kCpt][64]
-  const int wv = static_cast<int>(threadIdx.x >> 6);
-  auto q_slot = [&](int k, int j) -> u32x4& {
-    return q_lds[((wv * kCap + k) * C::kCpt + j) * kWave + lane];
-  };
-  float m[kCap], l[kCap], acc[kCap][C::kEpl];
 #pragma unroll
   for (int k = 0; k < kCap; ++k) {
-    m[k] = -INFINITY;
-    l[k] = 0.f;
-#pragma unroll
-    for (int e = 0; e < C::kEpl; ++e) acc[k][e] = 0.f;
-    if (k < nact) {
+    if (endk[k] > 0 && k % kGroupWaves == wv) {
       const T* qp = static_cast<const T*>(a.q) +
-                    (static_cast<int64_t>(base_seq + k) * a.num_heads + h) * D;
+                    (static_cast<int64_t>(lead + k) * a.num_heads + h) * D;
 #pragma unroll
       for (int j = 0; j < C::kCpt; ++j) q_slot(k, j) = ld16(qp + col(j));
     }
   }
+  __syncthreads();
 
-  // row offset of token (group_base + g) through the table entries b (group_base: a
-  // multiple of 8 relative to the partition start, wave-uniform)
-  auto row_offset = [&](const int (&b)[C::kTabRegs], int group_base) -> int64_t {
-    const int bi = group_base / BS;
-    int id;
-    if constexpr (C::kTabRegs == 1) {
-      id = __builtin_amdgcn_readlane(b[0], bi);
-    } else {
-      id = bi < kWave ? __builtin_amdgcn_readlane(b[0], bi)
-                      : __builtin_amdgcn_readlane(b[C::kTabRegs - 1], bi - kWave);
-    }
-    return (static_cast<int64_t>(id) * BS + (group_base % BS) + g) * row_stride;
-  };
-  // ALiBi (a compile-time variant: its registers would cost the plain runs a wave per SIMD
-  // at capacity 4): slope * (j - p) added to the score of token j for the member whose
-  // query sits at position p, dist = j - p (log2 units here)
+  const int64_t row_stride = static_cast<int64_t>(a.num_heads) * D;
+  const T* kbase = static_cast<const T*>(a.k_pool) + static_cast<int64_t>(h) * D;
+  const T* vbase = static_cast<const T*>(a.v_pool) + static_cast<int64_t>(h) * D;
+  // ALiBi (a compile-time variant): slope * (j - p) added to the score of token j for the
+  // member whose query sits at position p (log2 units here)
   const float slope = kAlibi ? a.alibi[h] * kLog2e : 0.f;
   auto score = [&](const u32x4 (&qv)[C::kCpt], const u32x4 (&kr)[C::kCpt], int dist) {
     float d = 0.f;
@@ -525,6 +520,14 @@ __global__ __launch_bounds__(64 * kHeadsPerWg) void decode_group_kernel(DecodeAr
     if constexpr (kAlibi) return fmaf(slope, static_cast<float>(dist), x);
     return x;
   };
+  float m[kCap], l[kCap], acc[kCap][C::kEpl];
+#pragma unroll
+  for (int k = 0; k < kCap; ++k) {
+    m[k] = -INFINITY;
+    l[k] = 0.f;
+#pragma unroll
+    for (int e = 0; e < C::kEpl; ++e) acc[k][e] = 0.f;
+  }
   auto update = [&](float& mk, float& lk, float (&ak)[C::kEpl], const float (&sc)[C::kG],
                     const u32x4 (&vr)[C::kG][C::kCpt], const bool (&ok)[C::kG]) {
     float mx = sc[0];
@@ -550,184 +553,193 @@ __global__ __launch_bounds__(64 * kHeadsPerWg) void decode_group_kernel(DecodeAr
     }
   };
 
-  // shared prefix: each row read once, every member updated from it.  Software-pipelined over
-  // two register buffers: the next trip's loads are in flight while a trip is computed (the
-  // loop is bound by one wave's chain of trips, so latency and arithmetic must overlap).
-  if (joint) {
-    bool all_ok[C::kG];
+  // item i (wave-uniform): member k (-1 = joint) and its first token relative to the partition
+  auto item = [&](int i, int& k, int& rel) {
+    k = -1;
+    rel = i * C::kTrip;
 #pragma unroll
-    for (int i = 0; i < C::kG; ++i) all_ok[i] = true;
-    auto load_trip = [&](int rel, u32x4 (&kr)[C::kG][C::kCpt], u32x4 (&vr)[C::kG][C::kCpt]) {
-      int64_t off[C::kG];
+    for (int kk = 0; kk < kCap; ++kk)
+      if (i >= pstart[kk] && i < pstart[kk + 1]) {
+        k = kk;
+        rel = t + (i - pstart[kk]) * C::kTrip;
+      }
+  };
+  // K and V rows of item i.  Every lane loads a row that holds a token of the member: a lane
+  // whose token lies past the member's end (a ragged last trip) reads the member's last token
+  // of its 8-token group instead (same block; its weight is zero), and a group wholly past the
+  // end reads the group holding the last token.  So the loads need no lane masks.
+  auto load = [&](int i, u32x4 (&kr)[C::kG][C::kCpt], u32x4 (&vr)[C::kG][C::kCpt]) {
+    int k, rel;
+    item(i, k, rel);
+    int wb[C::kTabRegs];
+    int end = t;
 #pragma unroll
-      for (int i = 0; i < C::kG; ++i) {
-        off[i] = row_offset(blk[0], rel + i * 8);
+    for (int r = 0; r < C::kTabRegs; ++r) wb[r] = fb[r];
 #pragma unroll
-        for (int j = 0; j < C::kCpt; ++j) kr[i][j] = ld_kv<false>(kbase + off[i] + col(j));
+    for (int kk = 0; kk < kCap; ++kk)
+      if (kk == k) {
+        end = endk[kk];
+#pragma unroll
+        for (int r = 0; r < C::kTabRegs; ++r) wb[r] = blk[kk][r];
       }
 #pragma unroll
-      for (int i = 0; i < C::kG; ++i)
-#pragma unroll
-        for (int j = 0; j < C::kCpt; ++j) vr[i][j] = ld_kv<false>(vbase + off[i] + col(j));
-    };
-    auto use_trip = [&](const u32x4 (&kr)[C::kG][C::kCpt], const u32x4 (&vr)[C::kG][C::kCpt],
-                        int rel) {
-#pragma unroll
-      for (int k = 0; k < kCap; ++k) {
-        if (k < nact) {
-          u32x4 qk[C::kCpt];
-#pragma unroll
-          for (int j = 0; j < C::kCpt; ++j) qk[j] = q_slot(k, j);
-          float sc[C::kG];
-#pragma unroll
-          for (int i = 0; i < C::kG; ++i)
-            sc[i] = score(qk, kr[i], start + rel + i * 8 + g - (ctxk[k] - 1));
-          update(m[k], l[k], acc[k], sc, vr, all_ok);
-        }
+    for (int i8 = 0; i8 < C::kG; ++i8) {
+      const int gb = min(rel + i8 * 8, (end - 1) / 8 * 8);  // wave-uniform
+      const int bi = gb / BS;
+      int id;
+      if constexpr (C::kTabRegs == 1) {
+        id = __builtin_amdgcn_readlane(wb[0], bi);
+      } else {
+        id = bi < kWave ? __builtin_amdgcn_readlane(wb[0], bi)
+                        : __builtin_amdgcn_readlane(wb[C::kTabRegs - 1], bi - kWave);
       }
-    };
-    const int ntrips = t / C::kTrip;  // >= 1
-    u32x4 ka[C::kG][C::kCpt], va[C::kG][C::kCpt], kb[C::kG][C::kCpt], vb[C::kG][C::kCpt];
-    load_trip(0, ka, va);
-    int trip = 0;
-    for (; trip + 2 <= ntrips; trip += 2) {
-      load_trip((trip + 1) * C::kTrip, kb, vb);
-      use_trip(ka, va, trip * C::kTrip);
-      // unconditional, so the wait for buffer b below never covers these loads; when the
-      // trips run out this re-reads the last one, unused
-      load_trip(min(trip + 2, ntrips - 1) * C::kTrip, ka, va);
-      use_trip(kb, vb, (trip + 1) * C::kTrip);
+      const int tok = min(gb + g, end - 1);
+      const int64_t off = (static_cast<int64_t>(id) * BS + tok % BS) * row_stride;
+#pragma unroll
+      for (int j = 0; j < C::kCpt; ++j) kr[i8][j] = ld_kv<false>(kbase + off + col(j));
     }
-    if (trip < ntrips) use_trip(ka, va, trip * C::kTrip);  // odd count: last trip in buffer a
-  }
-
-  // one member's own tokens [rel0, end) of the partition (table entries wb), then its result
-  auto finish = [&](const u32x4 (&wq)[C::kCpt], float& wm, float& wl, float (&wacc)[C::kEpl],
-                    const int (&wb)[C::kTabRegs], int rel0, int end, bool single, int seq,
-                    int qpos) {  // qpos: the member's query position, context length - 1
-    int rel = rel0;
-    for (; rel + C::kTrip <= end; rel += C::kTrip) {
-      u32x4 kr[C::kG][C::kCpt], vr[C::kG][C::kCpt];
-      int64_t off[C::kG];
-      bool ok[C::kG];
 #pragma unroll
-      for (int i = 0; i < C::kG; ++i) {
-        ok[i] = true;
-        off[i] = row_offset(wb, rel + i * 8);
-#pragma unroll
-        for (int j = 0; j < C::kCpt; ++j) kr[i][j] = ld_kv<false>(kbase + off[i] + col(j));
+    for (int i8 = 0; i8 < C::kG; ++i8) {
+      const int gb = min(rel + i8 * 8, (end - 1) / 8 * 8);
+      const int bi = gb / BS;
+      int id;
+      if constexpr (C::kTabRegs == 1) {
+        id = __builtin_amdgcn_readlane(wb[0], bi);
+      } else {
+        id = bi < kWave ? __builtin_amdgcn_readlane(wb[0], bi)
+                        : __builtin_amdgcn_readlane(wb[C::kTabRegs - 1], bi - kWave);
       }
+      const int tok = min(gb + g, end - 1);
+      const int64_t off = (static_cast<int64_t>(id) * BS + tok % BS) * row_stride;
 #pragma unroll
-      for (int i = 0; i < C::kG; ++i)
-#pragma unroll
-        for (int j = 0; j < C::kCpt; ++j) vr[i][j] = ld_kv<false>(vbase + off[i] + col(j));
-      float sc[C::kG];
-#pragma unroll
-      for (int i = 0; i < C::kG; ++i) sc[i] = score(wq, kr[i], start + rel + i * 8 + g - qpos);
-      update(wm, wl, wacc, sc, vr, ok);
+      for (int j = 0; j < C::kCpt; ++j) vr[i8][j] = ld_kv<false>(vbase + off + col(j));
     }
-    if (rel < end) {  // ragged last trip: lanes past the end load nothing
-      u32x4 kr[C::kG][C::kCpt], vr[C::kG][C::kCpt];
-      bool ok[C::kG];
+  };
+  // scores and running states of item i from its loaded rows
+  auto use = [&](int i, const u32x4 (&kr)[C::kG][C::kCpt], const u32x4 (&vr)[C::kG][C::kCpt]) {
+    int k, rel;
+    item(i, k, rel);
 #pragma unroll
-      for (int i = 0; i < C::kG; ++i) {
-        const int gb = rel + i * 8;
-        ok[i] = gb + g < end;
+    for (int kk = 0; kk < kCap; ++kk) {
+      if (endk[kk] > 0 && (k < 0 || k == kk)) {
+        u32x4 qk[C::kCpt];
 #pragma unroll
-        for (int j = 0; j < C::kCpt; ++j) {
-          kr[i][j] = u32x4{0, 0, 0, 0};
-          vr[i][j] = u32x4{0, 0, 0, 0};
+        for (int j = 0; j < C::kCpt; ++j) qk[j] = q_slot(kk, j);
+        float sc[C::kG];
+        bool ok[C::kG];
+#pragma unroll
+        for (int i8 = 0; i8 < C::kG; ++i8) {
+          const int tok = rel + i8 * 8 + g;
+          ok[i8] = tok < endk[kk];
+          const float x = score(qk, kr[i8], start + tok - (ctxk[kk] - 1));
+          sc[i8] = ok[i8] ? x : -INFINITY;
         }
-        if (gb < end) {  // wave-uniform: the group has at least one valid token
-          const int64_t off = row_offset(wb, gb);
-          if (ok[i]) {
-#pragma unroll
-            for (int j = 0; j < C::kCpt; ++j) kr[i][j] = ld_kv<false>(kbase + off + col(j));
-#pragma unroll
-            for (int j = 0; j < C::kCpt; ++j) vr[i][j] = ld_kv<false>(vbase + off + col(j));
-          }
-        }
-      }
-      float sc[C::kG];
-#pragma unroll
-      for (int i = 0; i < C::kG; ++i) {
-        const float x = score(wq, kr[i], start + rel + i * 8 + g - qpos);
-        sc[i] = ok[i] ? x : -INFINITY;
-      }
-      update(wm, wl, wacc, sc, vr, ok);
-    }
-
-    // merge the 8 token groups, then write the output (one partition) or the partial
-    const float M = wave_max(wm);
-    const float f = (wm == -INFINITY) ? 0.f : fast_exp2(wm - M);
-    wl *= f;
-#pragma unroll
-    for (int e = 0; e < C::kEpl; ++e) wacc[e] *= f;
-#pragma unroll
-    for (int x = 8; x < kWave; x <<= 1) {
-      wl += shfl_xor_f(wl, x);
-#pragma unroll
-      for (int e = 0; e < C::kEpl; ++e) wacc[e] += shfl_xor_f(wacc[e], x);
-    }
-    if (g != 0) return;
-    const int64_t row = static_cast<int64_t>(seq) * a.num_heads + h;
-    if (single) {
-      const float inv = 1.f / wl;
-      T* op = static_cast<T*>(a.out) + row * D;
-#pragma unroll
-      for (int j = 0; j < C::kCpt; ++j) {
-        float v[C::kEpc];
-#pragma unroll
-        for (int e = 0; e < C::kEpc; ++e) v[e] = wacc[j * C::kEpc + e] * inv;
-        store_chunk<T>(op + col(j), v);
-      }
-    } else {
-      const int64_t slot = row * a.num_parts_max + part;
-      float* wp = a.ws_acc + slot * D;
-#pragma unroll
-      for (int j = 0; j < C::kCpt; ++j)
-#pragma unroll
-        for (int e4 = 0; e4 < C::kEpc; e4 += 4) {
-          f32x4 v = {wacc[j * C::kEpc + e4], wacc[j * C::kEpc + e4 + 1],
-                     wacc[j * C::kEpc + e4 + 2], wacc[j * C::kEpc + e4 + 3]};
-          st16(wp + col(j) + e4, __builtin_bit_cast(u32x4, v));
-        }
-      if (c == 0) {
-        a.ws_ml[slot * 2] = M;
-        a.ws_ml[slot * 2 + 1] = wl;
+        update(m[kk], l[kk], acc[kk], sc, vr, ok);
       }
     }
   };
 
-  if (!joint) {  // this sequence alone: its table entries and length
-    int wb[C::kTabRegs];
-    int wctx = 0;
-#pragma unroll
-    for (int r = 0; r < C::kTabRegs; ++r) wb[r] = 0;
-#pragma unroll
-    for (int kk = 0; kk < kCap; ++kk) {
-      if (kk == s - lead) {
-        wctx = ctxk[kk];
-#pragma unroll
-        for (int r = 0; r < C::kTabRegs; ++r) wb[r] = blk[kk][r];
+  {
+    // three register buffers: the loads of this wave's next two items are in flight while an
+    // item is used (with few waves per SIMD, each wave must keep enough bytes in flight)
+    // Loads are issued unconditionally (past this wave's last item they re-read it, unused),
+    // so every wait for a buffer counts exactly the loads issued after it.
+    constexpr int S = kGroupWaves;
+    u32x4 ka[C::kG][C::kCpt], va[C::kG][C::kCpt], kb[C::kG][C::kCpt], vb[C::kG][C::kCpt];
+    u32x4 kc[C::kG][C::kCpt], vc[C::kG][C::kCpt];
+    int i = wv;
+    if (i < total) {
+      const int last = i + (total - 1 - i) / S * S;  // this wave's last item
+      auto nxt = [&](int j) { return j < total ? j : last; };
+      load(i, ka, va);
+      load(nxt(i + S), kb, vb);
+      for (; i < total; i += 3 * S) {
+        load(nxt(i + 2 * S), kc, vc);
+        use(i, ka, va);
+        if (i + S >= total) break;
+        load(nxt(i + 3 * S), ka, va);
+        use(i + S, kb, vb);
+        if (i + 2 * S >= total) break;
+        load(nxt(i + 4 * S), kb, vb);
+        use(i + 2 * S, kc, vc);
       }
     }
-    u32x4 wq[C::kCpt];
-#pragma unroll
-    for (int j = 0; j < C::kCpt; ++j) wq[j] = q_slot(0, j);
-    finish(wq, m[0], l[0], acc[0], wb, 0, min(wctx - start, P), wctx <= P, s, wctx - 1);
-    return;
   }
-  // each member's tokens past the shared prefix, then its result
+
+  // each wave's state per member: merge the 8 token groups, then to LDS
+  float* mrg_acc = reinterpret_cast<float*>(smem + kCap * C::kCpt * kWave);  // [W][kCap][D]
+  float* mrg_ml = mrg_acc + kGroupWaves * kCap * D;                          // [W][kCap][2]
 #pragma unroll
-  for (int k = 0; k < kCap; ++k)
-    if (k < nact) {
-      u32x4 wq[C::kCpt];
+  for (int k = 0; k < kCap; ++k) {
+    if (endk[k] > 0) {
+      const float M = wave_max(m[k]);
+      const float f = (m[k] == -INFINITY) ? 0.f : fast_exp2(m[k] - M);
+      float lk = l[k] * f;
+      float ak[C::kEpl];
 #pragma unroll
-      for (int j = 0; j < C::kCpt; ++j) wq[j] = q_slot(k, j);
-      finish(wq, m[k], l[k], acc[k], blk[k], t, min(ctxk[k] - start, P), ctxk[k] <= P,
-             lead + k, ctxk[k] - 1);
+      for (int e = 0; e < C::kEpl; ++e) ak[e] = acc[k][e] * f;
+#pragma unroll
+      for (int x = 8; x < kWave; x <<= 1) {
+        lk += shfl_xor_f(lk, x);
+#pragma unroll
+        for (int e = 0; e < C::kEpl; ++e) ak[e] += shfl_xor_f(ak[e], x);
+      }
+      if (g == 0) {
+        float* dst = mrg_acc + (wv * kCap + k) * D;
+#pragma unroll
+        for (int j = 0; j < C::kCpt; ++j)
+#pragma unroll
+          for (int e4 = 0; e4 < C::kEpc; e4 += 4) {
+            f32x4 v = {ak[j * C::kEpc + e4], ak[j * C::kEpc + e4 + 1], ak[j * C::kEpc + e4 + 2],
+                       ak[j * C::kEpc + e4 + 3]};
+            *reinterpret_cast<f32x4*>(dst + col(j) + e4) = v;
+          }
+        if (c == 0) {
+          mrg_ml[(wv * kCap + k) * 2] = M;
+          mrg_ml[(wv * kCap + k) * 2 + 1] = lk;
+        }
+      }
     }
+  }
+  __syncthreads();
+
+  // per member: combine the waves' states, then its output (a context within one partition)
+  // or its partial for the merge pass
+#pragma unroll
+  for (int k = 0; k < kCap; ++k) {
+    if (endk[k] == 0) continue;
+    float Mw[kGroupWaves];
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kGroupWaves; ++w) {
+      Mw[w] = mrg_ml[(w * kCap + k) * 2];
+      M = fmaxf(M, Mw[w]);
+    }
+    float wt[kGroupWaves];
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kGroupWaves; ++w) {
+      wt[w] = Mw[w] == -INFINITY ? 0.f : fast_exp2(Mw[w] - M);
+      L = fmaf(wt[w], mrg_ml[(w * kCap + k) * 2 + 1], L);
+    }
+    const int64_t row = static_cast<int64_t>(lead + k) * a.num_heads + h;
+    const bool single = ctxk[k] <= P;
+    for (int d = threadIdx.x; d < D; d += 64 * kGroupWaves) {
+      float o = 0.f;
+#pragma unroll
+      for (int w = 0; w < kGroupWaves; ++w) o = fmaf(wt[w], mrg_acc[(w * kCap + k) * D + d], o);
+      if (single) {
+        static_cast<T*>(a.out)[row * D + d] = static_cast<T>(o / L);
+      } else {
+        const int64_t slot = row * a.num_parts_max + part;
+        a.ws_acc[slot * D + d] = o;
+        if (d == 0) {
+          a.ws_ml[slot * 2] = M;
+          a.ws_ml[slot * 2 + 1] = L;
+        }
+      }
+    }
+  }
 }
 
 size_t decode_workspace_bytes(int64_t num_tokens, int64_t num_heads, int64_t head_dim,
@@ -817,11 +829,13 @@ static hipError_t launch_group_t(const DecodeArgs& a0, int max_context_len, hipS
   a.num_parts_max = workspace_parts(max_context_len);
   a.ws_acc = static_cast<float*>(a.workspace);
   a.ws_ml = a.ws_acc + static_cast<int64_t>(a.num_tokens) * a.num_heads * a.num_parts_max * D;
-  a.heads_per_wg = a.num_heads % kHeadsPerWg == 0 ? kHeadsPerWg : 1;
-  const dim3 grid1(a.num_heads / a.heads_per_wg, a.num_seqs, nparts);
-  const size_t q_bytes = static_cast<size_t>(a.heads_per_wg) * kCap * (D * 2 / 128) * kWave * 16;
+  const int runs = (a.num_seqs + a.group - 1) / a.group;
+  const dim3 grid1(a.num_heads, runs, nparts);
+  // LDS: the members' query chunks (one per lane slot) and the waves' states for the merge
+  const size_t lds = static_cast<size_t>(kCap) * (D * 2 / 128) * kWave * 16 +
+                     static_cast<size_t>(kGroupWaves) * kCap * (D + 2) * 4;
   hipLaunchKernelGGL((decode_group_kernel<D, BS, P, kCap, kAlibi>), grid1,
-                     dim3(kWave * a.heads_per_wg), q_bytes, stream, a);
+                     dim3(kWave * kGroupWaves), lds, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nparts <= 1) return err;
   hipLaunchKernelGGL((decode_merge_kernel<f16, D>), dim3(a.num_heads, a.num_seqs), dim3(kWave), 0,
@@ -842,26 +856,32 @@ static hipError_t launch_group_cap(const DecodeArgs& a, int max_context_len, hip
   return launch_group_cap<D, BS, P, false>(a, max_context_len, stream);
 }
 
-// Grouped decode partition: the largest of 1024, 512, 256 tokens for which runs x heads x
-// partitions of the longest context reach kGroupTargetWaves, about 1.5 joint waves per SIMD.
-// Measured: 16 runs of 6 samples x 40 heads, contexts ~1,000-1,300, is fastest at 512 (137 us;
-// 256: 159, 1024: 178); 64 runs of 4 beams x 40 heads, contexts 1,024-4,096, at 1024.
-constexpr int64_t kGroupTargetWaves = 1536;
+// Grouped decode partition: the largest of 2048 (block size >= 16), 1024 and 512 tokens for
+// which runs x heads x partitions of the longest context reach kGroupTargetWgs workgroups
+// (about two rounds of the chip at two workgroups per CU), else 512.  Longer partitions give
+// each wave more items for the same per-workgroup set-up and merge.  Measured on MI355X:
+// 16 runs of 6 samples x 40 heads (contexts up to ~1,300) fastest at 1024; the same batch at
+// 5 heads at 512; 64 runs of 4 or 6 beams x 40 heads (contexts up to ~4,200) at 2048.
+constexpr int64_t kGroupTargetWgs = 1024;
 
-static int pick_group_partition(const DecodeArgs& a, int max_context_len) {
+static int pick_group_partition(const DecodeArgs& a, int block_size, int max_context_len) {
   const int64_t units =
       static_cast<int64_t>((a.num_seqs + a.group - 1) / a.group) * a.num_heads;
-  int p = 1024;
-  while (p > 256 && units * ((max_context_len + p - 1) / p) < kGroupTargetWaves) p >>= 1;
+  int p = block_size == 8 ? 1024 : 2048;
+  while (p > 512 && units * ((max_context_len + p - 1) / p) < kGroupTargetWgs) p >>= 1;
   return p;
 }
 
 template <int D, int BS>
 static hipError_t launch_group_p(const DecodeArgs& a, int max_context_len, hipStream_t stream) {
-  const int p = pick_group_partition(a, max_context_len);
-  if (p <= 256) return launch_group_cap<D, BS, 256>(a, max_context_len, stream);
+  const int p = pick_group_partition(a, BS, max_context_len);
   if (p <= 512) return launch_group_cap<D, BS, 512>(a, max_context_len, stream);
-  return launch_group_cap<D, BS, 1024>(a, max_context_len, stream);
+  if constexpr (BS == 8) {
+    return launch_group_cap<D, BS, 1024>(a, max_context_len, stream);
+  } else {
+    if (p <= 1024) return launch_group_cap<D, BS, 1024>(a, max_context_len, stream);
+    return launch_group_cap<D, BS, 2048>(a, max_context_len, stream);
+  }
 }
 
 // Grouped decode (fp16, no window, one query per sequence; checked by the caller).

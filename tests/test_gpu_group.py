@@ -136,8 +136,8 @@ def test_group_short_contexts_single_partition():
 
 def test_group_early_divergence_long_tails():
     """Prompts that end early in a partition followed by long own tails: the partition starts
-    shared, but the members' remainders are too long for the joint path and each member reads
-    its own rows; shared partitions before it still run jointly."""
+    with joint trips, then every member's long remainder is read through its own entries (as
+    items dealt over the workgroup's waves); shared partitions before it are wholly joint."""
     log("[case] early divergence")
     rng = np.random.default_rng(13)
     tails = [list(rng.integers(200, 700, size=6)) for _ in range(3)]
@@ -147,9 +147,9 @@ def test_group_early_divergence_long_tails():
 
 @pytest.mark.parametrize("lo,hi,B", [(1500, 2000, 16), (3500, 4000, 8)])
 def test_group_larger_partitions_sampled(lo, hi, B):
-    """Batches large enough for longer partitions (16 runs of 4 x 32 heads = 512 joint units):
-    contexts up to ~2,000 take 512-token partitions, up to ~4,000 take 1024-token ones (with
-    B = 8: 128 table entries, two per lane).  Sampled sequences against the oracle."""
+    """Batches with longer contexts (16 runs of 4 x 32 heads): contexts up to ~2,000 and ~4,000
+    take 1024- or 2048-token partitions (with B = 8: at most 1024, 128 table entries, two per
+    lane).  Sampled sequences against the oracle."""
     log(f"[case] longer partitions: prompts U{{{lo}..{hi}}} B={B}")
     rng = np.random.default_rng(lo + B)
     prompts = list(rng.integers(lo, hi, size=16))
