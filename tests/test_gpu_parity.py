@@ -510,3 +510,15 @@ def test_chunk_only_batch():
     """Every sequence is a chunk (no decode units); the tile kernel alone writes the output."""
     w = make_custom_mixed(42, 2, 16, [(64, 64), (5, 128), (0, 256)], [], name="chunks_only")
     full_check(w)
+
+
+@pytest.mark.parametrize("head_dim,B", [(128, 16), (128, 8), (64, 32), (64, 16)])
+def test_mixed_batch_32_heads(head_dim, B):
+    """Mixed batches large enough that the tile launch needs no key splits (32 heads, >= 2,000
+    chunk rows): chunks over priors of 0..1,000 tokens ending mid-block, decodes of 1..3,000
+    tokens; every sequence against the oracle."""
+    chunks = [(0, 512), (300, 512), (1000, 520), (37, 600)]
+    decodes = [1, 17, 256, 257, 1500, 2049, 3000]
+    w = make_custom_mixed(70 + B + head_dim, 32, B, chunks, decodes,
+                          name=f"mixed_32h_d{head_dim}_B{B}", head_dim=head_dim)
+    every_sequence_check(w)
