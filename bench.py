@@ -2,12 +2,12 @@
 """Throughput of the paged KV-cache hot path on one MI355X.
 
 One step = the whole path over one batch: pa_write_kv appends this step's
-token per sequence into its cache slot, then pa_decode (context partitions +
-merge pass) computes paged attention for every (sequence, head).  Default
-batch: 256 sequences x 40 heads, head_dim 128, block size 16, fp16 K/V/q with
-fp32 accumulation, context lengths U{1024..4096} before the append, a shared
-pool of 47,104 blocks (15.4 GB of K+V), synthetic seeded data already resident
-in HBM.
+token per sequence into its cache slot, then pa_decode (longest-first order,
+context partitions + merge pass) computes paged attention for every (sequence,
+head).  Default batch: 256 sequences x 40 heads, head_dim 128, block size 16,
+fp16 K/V/q with fp32 accumulation, context lengths U{1024..4096} before the
+append, a shared pool of 47,104 blocks (15.4 GB of K+V), synthetic seeded data
+already resident in HBM.
 
 Printed (one JSON line): K/V GB/s read = algorithmic K/V bytes of the step
 (every valid K and V row of every sequence once) / wall time per step; plus
@@ -912,7 +912,7 @@ def main(argv=None) -> int:
                               round(float(np.percentile(dec, 90)), 4)],
         "write_ms": round(write_ms, 4),
         "roofline": {
-            "kernel": "pa_decode (partition pass + merge pass)",
+            "kernel": "pa_decode (order + partition pass + merge pass)",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,

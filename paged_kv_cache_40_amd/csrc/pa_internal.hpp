@@ -32,6 +32,8 @@ struct DecodeArgs {
   int32_t group;           // > 1: consecutive runs of this many sequences may share blocks
   void* workspace;         // caller's scratch (see decode_workspace_bytes)
   // set by the launcher:
+  const int32_t* order;    // nullptr, or the sequence each grid row of pass 1 takes
+                           // (longest context first), in the workspace
   int32_t heads_per_wg;    // waves (one head each) per workgroup
   int32_t num_parts_max;   // partition slots per (query row, head) in the workspace
   int32_t part_size;       // tokens per context partition

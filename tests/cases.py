@@ -1,8 +1,10 @@
-"""Batches shared by a GPU parity test and the CPU test that shows how sharp it is.
-
-Defined once here so the CPU side (tests/test_sensitivity.py) reasons about exactly
-the inputs the GPU side (tests/test_gpu_parity.py) runs.
+"""Batches shared by several tests: the marked long-context cases, shared by a GPU parity
+test and the CPU test that shows how sharp it is (defined once here so the CPU side,
+tests/test_sensitivity.py, reasons about exactly the inputs the GPU side,
+tests/test_gpu_parity.py, runs), and the lengths of the longest-first dispatch cases.
 """
+
+import numpy as np
 
 from workloads import make_custom_decode, make_custom_mixed
 
@@ -28,3 +30,13 @@ def long_chunk_marked():
     """A 300-query chunk over a 30,000-token prior and a short chunk, next to decodes."""
     return make_custom_mixed(82, 2, 16, [(30000, 300), (5, 40)], [20000, 9],
                              name="long_chunk_marked", **CHUNK_MARK)
+
+
+def ordered_lens(seed, n, long_len):
+    """Context lengths with many equal values and a few long ones: a batch whose bound
+    (sequences x heads x longest context x K and V bytes) makes the library dispatch the
+    sequences longest first, so that ties and the rank computation are exercised."""
+    rng = np.random.default_rng(seed)
+    lens = rng.choice([1, 2, 15, 16, 17, 255, 256, 257, 1000], size=n).astype(np.int32)
+    lens[[3, n // 2, n - 1]] = long_len
+    return lens

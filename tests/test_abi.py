@@ -53,8 +53,9 @@ def test_strerror(lib):
 def test_workspace_bytes(lib):
     f = lib.pa_decode_workspace_bytes
     assert f(256, 40, 128, 256) == 0               # one partition: no partials
-    assert f(256, 40, 128, 257) == 256 * 40 * 2 * 130 * 4
-    assert f(256, 40, 128, 4097) == 256 * 40 * 17 * 130 * 4
+    # partials, then one int per query row (the longest-first order of the sequences)
+    assert f(256, 40, 128, 257) == 256 * 40 * 2 * 130 * 4 + 256 * 4
+    assert f(256, 40, 128, 4097) == 256 * 40 * 17 * 130 * 4 + 256 * 4
     assert f(0, 40, 128, 4097) == 0
 
 

@@ -26,6 +26,7 @@ import torch
 import oracle
 from paged_kv_cache_40_amd import api
 from workloads import make_custom_decode, make_custom_mixed
+from cases import ordered_lens
 from paged_harness import (assert_bits_equal, assert_close, host_copy, log, oracle_step,
                            run_library)
 
@@ -197,5 +198,15 @@ def test_malformed_decode_batch(dtype, head_dim, block_size):
     lens = [3, 40, 257, 1000, 2049, 9, 600, 128]
     w = make_custom_decode(72 + block_size, dtype, 3, head_dim, block_size, lens,
                            write_one=True, name=f"malformed_decode_{dtype}_B{block_size}")
+    order = sorted(range(w.num_seqs), key=lambda s: -int(w.context_lens[s]))
+    malformed_check(w, order[:5], [])
+
+
+def test_malformed_decode_batch_ordered():
+    """A batch large enough by its bound (600 sequences x 8 heads, 5000-token bound) for pass 1
+    to take the sequences longest first: the broken lengths (0, negative, INT_MAX, past the
+    used entries) go through the ordering too."""
+    w = make_custom_decode(93, "f16", 8, 128, 32, ordered_lens(93, 600, 5000), write_one=True,
+                           name="malformed_decode_ordered")
     order = sorted(range(w.num_seqs), key=lambda s: -int(w.context_lens[s]))
     malformed_check(w, order[:5], [])
