@@ -757,26 +757,46 @@ size_t decode_workspace_bytes(int64_t num_tokens, int64_t num_heads, int64_t hea
 
 // Longest-first order of the sequences for pass 1 [a scheduling choice, not part of the
 // method: the partitions of the longest contexts start first, so the launch does not end on
-// them].  One workgroup: sequence t gets rank = the number of sequences with a longer clamped
-// context, or an equal one and a smaller index (a strict total order, so the ranks are a
-// permutation), and order[rank] = t.  Each of S threads compares with all S lengths in LDS.
+// them].  Sequence j's key is (clamped length << 32) | ~j: keys are distinct, and a larger key
+// means a longer context, or an equal one and a smaller index.  Sequence t's rank = the number
+// of keys above its own (so the ranks are a permutation), and order[rank] = t.  Workgroup b
+// ranks sequences 64b..64b+63, one per lane; each of its four waves counts over a quarter of
+// the keys (staged in LDS), and the quarters' counts are summed in LDS.
 constexpr int kOrderMaxSeqs = 1024;
+constexpr int kOrderWaves = 4;
 
-__global__ __launch_bounds__(kOrderMaxSeqs) void decode_order_kernel(const int32_t* context_lens,
-                                                                     int num_seqs, int cap,
-                                                                     int32_t* order) {
-  __shared__ int len[kOrderMaxSeqs];
-  const int t = threadIdx.x;
-  if (t < num_seqs) len[t] = min(max(context_lens[t], 0), cap);
-  __syncthreads();
-  if (t >= num_seqs) return;
-  const int mine = len[t];
-  int rank = 0;
-  for (int j = 0; j < num_seqs; ++j) {
-    const int o = len[j];
-    rank += (o > mine || (o == mine && j < t)) ? 1 : 0;
+__global__ __launch_bounds__(kWave * kOrderWaves) void decode_order_kernel(
+    const int32_t* context_lens, int num_seqs, int cap, int32_t* order) {
+  __shared__ uint64_t key[kOrderMaxSeqs];
+  __shared__ int part[kOrderWaves][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // slots past num_seqs (up to the quarter boundary) hold 0, below every real key
+  const int quarter = ((num_seqs + kOrderWaves - 1) / kOrderWaves + 7) & ~7;
+  for (int j = threadIdx.x; j < quarter * kOrderWaves; j += kWave * kOrderWaves) {
+    uint64_t k = 0;
+    if (j < num_seqs) {
+      const uint32_t len = static_cast<uint32_t>(min(max(context_lens[j], 0), cap));
+      k = (static_cast<uint64_t>(len) << 32) | static_cast<uint32_t>(~j);
+    }
+    key[j] = k;
   }
-  order[rank] = t;
+  __syncthreads();
+  const int t = blockIdx.x * kWave + lane;
+  const uint64_t mine = t < num_seqs ? key[t] : ~0ull;
+  int count = 0;
+  for (int j0 = wv * quarter; j0 < (wv + 1) * quarter; j0 += 8) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) count += key[j0 + e] > mine ? 1 : 0;
+  }
+  part[wv][lane] = count;
+  __syncthreads();
+  if (wv == 0 && t < num_seqs) {
+    int rank = 0;
+#pragma unroll
+    for (int w = 0; w < kOrderWaves; ++w) rank += part[w][lane];
+    order[rank] = t;
+  }
 }
 
 // Order the sequences longest first when the launch is long enough for its tail to matter
@@ -821,7 +841,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a0, int max_context_len, hip
           a.ws_ml + static_cast<int64_t>(a.num_tokens) * a.num_heads * a.num_parts_max * 2);
       const int cap = static_cast<int>(
           std::min<int64_t>(static_cast<int64_t>(a.max_blocks) * BS, max_context_len));
-      hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kOrderMaxSeqs), 0, stream,
+      const unsigned wgs = static_cast<unsigned>((a.num_seqs + kWave - 1) / kWave);
+      hipLaunchKernelGGL(decode_order_kernel, dim3(wgs), dim3(kWave * kOrderWaves), 0, stream,
                          a.context_lens, a.num_seqs, cap, order);
       a.order = order;
     }
