@@ -70,7 +70,8 @@ def test_full_size_large_batch_marked():
 def test_longest_first_order_with_ties():
     """600 sequences x 8 heads with a 5000-token bound (12 GB of K/V by the bound, above the
     4 GB at which pass 1 takes the sequences longest first): every sequence against the
-    oracle, and bit-identical to the shared-blocks launch, which keeps the given order."""
+    oracle, bit-identical to the shared-blocks launch, which keeps the given order, and
+    captured in a HIP graph, bit-identical on every replay."""
     w = make_custom_decode(91, "f16", 8, 128, 16, ordered_lens(91, 600, 5000), write_one=True,
                            name="ordered_ties")
     assert w.num_seqs * w.num_heads * w.max_context_len * 2 * 128 * 2 >= 4e9
@@ -82,6 +83,36 @@ def test_longest_first_order_with_ties():
     torch.cuda.synchronize()
     assert torch.equal(plain.view(torch.int16), hinted.view(torch.int16))
     log("[ok] bit-identical to the launch in the given order")
+    # the same call captured in a HIP graph: the order is recomputed on every replay (the
+    # workspace is zeroed before each one, which would send every grid row of the partition
+    # pass to sequence 0 if it were not)
+    need = api.pa_decode_workspace_bytes(w.num_queries, w.num_heads, w.head_dim,
+                                         w.max_context_len)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(t1["q"])
+
+    def call():
+        api.pa_decode(out, t1["q"], t1["k_pool"], t1["v_pool"], t1["block_tables"],
+                      t1["context_lens"], max_context_len=w.max_context_len, workspace=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), plain.view(torch.int16)), "eager call"
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for i in range(3):
+        ws.zero_()
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), plain.view(torch.int16)), f"replay {i}"
+    log("[ok] 3 graph replays bit-identical")
 
 
 # ------------------------------------------------------- layouts, edges --
