@@ -802,8 +802,9 @@ __global__ __launch_bounds__(kWave * kOrderWaves) void decode_order_kernel(
 // Order the sequences longest first when the launch is long enough for its tail to matter
 // (measured on MI355X: 256 sequences x 40 heads with contexts U{1025..4097}, 13.4 GB: 1.99 vs
 // 2.07 ms; 64 sequences x 40 heads, lognormal lengths, 1 GB: within 1%, less than the extra
-// launch costs): at least kOrderMinBytes of K/V as bounded by the longest span read, and more
-// than one partition.
+// launch costs): at least kOrderMinBytes of K/V as bounded by the longest context, more than
+// one partition, and no sliding window (a window caps every sequence's span, so the lengths
+// stop mattering: the same large batch with a 1,024-token window, 0.845 ms ordered vs 0.836).
 constexpr double kOrderMinBytes = 4e9;
 
 // Longest token span one (sequence, head) reads: the context, or with a sliding window
@@ -832,10 +833,10 @@ static hipError_t launch_decode_t(const DecodeArgs& a0, int max_context_len, hip
     hipLaunchKernelGGL((decode_partition_kernel<T, D, BS, P, true>), grid1, block1, 0, stream,
                        a);
   } else {
-    const double bound = static_cast<double>(a.num_seqs) * a.num_heads *
-                         decode_span(a, BS, max_context_len) * 2.0 * D * sizeof(T);
+    const double bound =
+        static_cast<double>(a.num_seqs) * a.num_heads * max_context_len * 2.0 * D * sizeof(T);
     // the order takes num_seqs of the num_tokens ints after the partials
-    if (a.workspace != nullptr && nparts > 1 && a.num_seqs > 1 &&
+    if (a.workspace != nullptr && a.window <= 0 && nparts > 1 && a.num_seqs > 1 &&
         a.num_seqs <= kOrderMaxSeqs && a.num_seqs <= a.num_tokens && bound >= kOrderMinBytes) {
       int32_t* order = reinterpret_cast<int32_t*>(
           a.ws_ml + static_cast<int64_t>(a.num_tokens) * a.num_heads * a.num_parts_max * 2);
