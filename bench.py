@@ -33,7 +33,8 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "paged decode attention: K/V GB/s read & % of HBM peak; seq-heads/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_decode_traffic.json")
 DECODE_SOURCES = ["paged_kv_cache_40_amd/csrc/pa_decode.hip",
-                  "paged_kv_cache_40_amd/csrc/pa_common.hpp"]
+                  "paged_kv_cache_40_amd/csrc/pa_common.hpp",
+                  "paged_kv_cache_40_amd/csrc/pa_internal.hpp"]
 
 
 def decode_source_hash() -> str:

@@ -20,7 +20,7 @@
 // the order the threads run in.  Collisions use two bits per slot (or block): the first
 // pass sets "seen" and, for a second visitor, "shared"; the second pass reports every
 // visitor of a shared slot, the lowest of which the minimum keeps.
-// Every load is bounds-checked before use, so malformed inputs cannot fault the checker.
+// Every load is bounds-checked before use, so malformed inputs cannot fault these kernels.
 
 #include "../../include/pa.h"
 #include "pa_common.hpp"

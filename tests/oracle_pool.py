@@ -16,7 +16,7 @@ import tempfile
 
 import numpy as np
 
-# The GPU machine gives a process a share of 16 host cores whatever the machine reports.
+# One GPU's share of a host is 16 cores, whatever the machine reports: never more workers.
 MAX_WORKERS = 16
 
 

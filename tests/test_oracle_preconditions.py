@@ -1,7 +1,7 @@
 """Pins of oracle.preconditions (CPU).
 
 Each case is a tiny batch built by hand with the verdict written out by hand
-from the definitions (not by running the checker); batches that a block
+from the definitions (not by running the check functions); batches that a block
 manager builds by forks, appends and copy-on-write must pass every check.
 """
 
