@@ -115,6 +115,24 @@ def test_longest_first_order_with_ties():
     log("[ok] 3 graph replays bit-identical")
 
 
+@pytest.mark.parametrize("S", [1024, 1025])
+def test_longest_first_order_at_the_sequence_limit(S):
+    """1,024 sequences (the most the order kernel ranks) and 1,025 (the given order) x 8 heads
+    with a 1,000-token bound (4.2 GB by the bound): every sequence against the oracle, and
+    bit-identical to the shared-blocks launch."""
+    w = make_custom_decode(92, "f16", 8, 128, 16, ordered_lens(92, S, 1000), write_one=True,
+                           name=f"ordered_{S}")
+    assert w.num_seqs * w.num_heads * w.max_context_len * 2 * 128 * 2 >= 4e9
+    every_sequence_check(w)
+    t1 = w.device_tensors("cuda")
+    plain = run_library(w, t1)
+    t2 = w.device_tensors("cuda")
+    hinted = run_library(w, t2, shared=True)
+    torch.cuda.synchronize()
+    assert torch.equal(plain.view(torch.int16), hinted.view(torch.int16))
+    log("[ok] bit-identical to the launch in the given order")
+
+
 # ------------------------------------------------------- layouts, edges --
 
 EDGE_LENS = [1, 2, 7, 8, 9, 15, 16, 17, 31, 32, 33, 255, 256, 257, 511, 512, 513, 1000, 2049]
