@@ -1,7 +1,8 @@
 """pa_decode_noalloc (the workspace in the library's own device array) through the C ABI
 against pa_decode_ext with a caller workspace: the same kernels, so the same bits, on two
-calls in a row - the second with a smaller batch - and on a batch that also takes the
-chunked-prefill tile path's key splits.  The first call is also checked against the oracle."""
+calls in a row - the second with a smaller batch - on a batch that also takes the
+chunked-prefill tile path's key splits, and on one whose partition pass takes the sequences
+longest first.  The first call is also checked against the oracle."""
 
 import numpy as np
 import pytest
@@ -66,6 +67,20 @@ def test_noalloc_chunks_with_key_splits_and_variants():
     g = make_custom_decode(94, "f16", 4, 128, 16, [3000, 2990, 2500, 1800], name="noalloc_group")
     tg = g.device_tensors("cuda")
     out_n, out_e = _ext_and_noalloc(g, tg, group=2)
+    assert _same_bits(out_n, out_e)
+    log("[ok]")
+
+
+def test_noalloc_longest_first_batch():
+    """A batch large enough by its bound (600 sequences x 8 heads, 5,000-token bound) for the
+    partition pass to take the sequences longest first: the order lives in the array too."""
+    from cases import ordered_lens
+    w = make_custom_decode(96, "f16", 8, 128, 16, ordered_lens(96, 600, 5000),
+                           name="noalloc_ordered")
+    assert w.num_seqs * w.num_heads * w.max_context_len * 2 * 128 * 2 >= 4e9
+    log(f"[case] {w.name}")
+    t = w.device_tensors("cuda")
+    out_n, out_e = _ext_and_noalloc(w, t)
     assert _same_bits(out_n, out_e)
     log("[ok]")
 
