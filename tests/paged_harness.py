@@ -256,24 +256,24 @@ def moved_slots_check(w, t, k_before, v_before):
     assert moved == expect
 
 
-def every_sequence_check(w, group=0, margins=False, min_margin=3.0):
+def every_sequence_check(w, group=0, margins=False, min_margin=3.0, window=0, alibi=None):
     """The full batch as bench.py runs it, every sequence and head against the oracle (in a
     pool of host processes), the pools bit for bit over every block the batch reads, and a
     whole-pool check that only the expected slots moved.  With margins, also shows on these
     very inputs that leaving out any one block of any decode sequence would break the
     tolerance (tests/sensitivity.py)."""
     log(f"[case] full {w.name} S={w.num_seqs} H={w.num_heads} NB={w.num_blocks} group={group} "
-        f"k_scale={w.k_scale} v_mark={w.v_mark}")
+        f"window={window} alibi={alibi is not None} k_scale={w.k_scale} v_mark={w.v_mark}")
     t = w.device_tensors("cuda")
     seqs = list(range(w.num_seqs))
     sub = snapshot_for(w, t, seqs)
     k_before = t["k_pool"].clone()
     v_before = t["v_pool"].clone()
-    out = run_library(w, t, group=group)
+    out = run_library(w, t, group=group, window=window, alibi=alibi)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     log("[step] library done; oracle over every sequence")
-    refs, m = oracle_every_sequence(w, sub, margins=margins)
+    refs, m = oracle_every_sequence(w, sub, window=window, alibi=alibi, margins=margins)
     worst = 0.0
     for i, s in enumerate(seqs):
         worst = max(worst, assert_close(got[sub["q_rows"][i]], refs[s], w.dtype,

@@ -13,8 +13,8 @@ import torch
 
 from paged_kv_cache_40_amd import api
 from workloads import make_config, make_custom_decode, make_custom_mixed
-from paged_harness import (assert_bits_equal, assert_close, host_copy, log, oracle_step,
-                           oracle_sub, pick_sequences, run_library, snapshot_for)
+from paged_harness import (assert_bits_equal, assert_close, every_sequence_check, host_copy, log,
+                           oracle_step, oracle_sub, pick_sequences, run_library, snapshot_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -135,22 +135,12 @@ def test_window_partitions_sampled(S, H, lo, hi, W):
     log("[ok]")
 
 
-def test_full_size_large_batch_window_alibi_sampled():
+def test_full_size_large_batch_window_alibi_every_sequence():
     """The 256-sequence, 40-head large-batch decode (contexts 1025..4097) with a 1024-token
-    window and ALiBi, as the benchmark's variant line runs it; sampled sequences, every head."""
+    window and ALiBi, as the benchmark's variant line runs it: every sequence and head
+    against the oracle (in a pool of host processes), the pools bit for bit."""
     w = make_config(5)
-    W = 1024
-    slopes = geometric_slopes(w.num_heads)
-    log(f"[case] full {w.name} W={W} alibi")
-    t = w.device_tensors("cuda")
-    seqs = pick_sequences(w, n=4, seed=9)
-    sub = snapshot_for(w, t, seqs)
-    out = run_library(w, t, window=W, alibi=slopes)
-    torch.cuda.synchronize()
-    refs, _, _ = oracle_sub(w, sub, window=W, alibi=slopes)
-    for i, s in enumerate(seqs):
-        assert_close(out[s:s + 1].cpu().numpy(), refs[i], w.dtype, f"{w.name} seq {s}")
-    log("[ok]")
+    every_sequence_check(w, window=1024, alibi=geometric_slopes(w.num_heads))
 
 
 # ------------------------------------------- chunked prefill (multi-query tile path) --
