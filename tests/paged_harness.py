@@ -256,6 +256,16 @@ def moved_slots_check(w, t, k_before, v_before):
     assert moved == expect
 
 
+# Largest K+V pool that the every-sequence check copies to the host and shares with its
+# worker processes; larger batches are checked on sampled sequences.
+FULL_CHECK_POOL_BYTES = 16 << 30
+
+
+def pool_bytes(w) -> int:
+    elt = 2 if w.dtype == "f16" else 4
+    return 2 * w.num_blocks * w.block_size * w.num_heads * w.head_dim * elt
+
+
 def every_sequence_check(w, group=0, margins=False, min_margin=3.0, window=0, alibi=None):
     """The full batch as bench.py runs it, every sequence and head against the oracle (in a
     pool of host processes), the pools bit for bit over every block the batch reads, and a

@@ -13,8 +13,9 @@ import torch
 
 from paged_kv_cache_40_amd import api
 from workloads import make_config, make_custom_decode, make_custom_mixed
-from paged_harness import (assert_bits_equal, assert_close, every_sequence_check, host_copy, log,
-                           oracle_step, oracle_sub, pick_sequences, run_library, snapshot_for)
+from paged_harness import (FULL_CHECK_POOL_BYTES, assert_bits_equal, assert_close,
+                           every_sequence_check, host_copy, log, oracle_step, oracle_sub,
+                           pick_sequences, pool_bytes, run_library, snapshot_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -108,13 +109,14 @@ def test_neutral_variants_bit_identical_to_plain():
     log("[ok]")
 
 
-# Windows long enough to span several context partitions of each size the launch picks.
+# Windows long enough to span several context partitions of each size the launch picks; every
+# sequence when the pools fit the host-side oracle comfortably, else sampled sequences.
 @pytest.mark.parametrize("S,H,lo,hi,W", [
     (64, 40, 3000, 9000, 2500),    # 256-token partitions inside the window
     (256, 40, 1025, 4097, 4000),   # 2048-token partitions; short contexts end before W
     (256, 40, 1025, 4097, 1024),   # 1024-token partitions
 ])
-def test_window_partitions_sampled(S, H, lo, hi, W):
+def test_window_partitions(S, H, lo, hi, W):
     rng = np.random.default_rng(S + W)
     lens = rng.integers(lo, hi + 1, size=S)
     lens[0], lens[-1] = lo, hi
@@ -122,6 +124,9 @@ def test_window_partitions_sampled(S, H, lo, hi, W):
                            name=f"window_{W}_S{S}")
     slopes = geometric_slopes(H)
     log(f"[case] {w.name} L=[{lo},{hi}] W={W} NB={w.num_blocks}")
+    if pool_bytes(w) <= FULL_CHECK_POOL_BYTES:
+        every_sequence_check(w, window=W, alibi=slopes)
+        return
     t = w.device_tensors("cuda")
     seqs = pick_sequences(w, n=3, seed=S)
     sub = snapshot_for(w, t, seqs)
