@@ -116,6 +116,18 @@ def test_longest_first_order_with_ties():
     log("[ok] 3 graph replays bit-identical")
 
 
+def test_longest_first_order_in_a_mixed_batch():
+    """Chunks of several queries among 400 decodes (8 heads, a 5,000-token bound): the order
+    ranks every sequence, the partition pass skips the chunks and the tile path takes them;
+    every sequence against the oracle."""
+    lens = ordered_lens(94, 400, 5000)
+    w = make_custom_mixed(94, 8, 16, [(0, 300), (2000, 128), (4800, 200)], list(lens),
+                          name="ordered_mixed")
+    assert w.num_seqs <= w.num_queries
+    assert w.num_seqs * w.num_heads * w.max_context_len * 2 * 128 * 2 >= 4e9
+    every_sequence_check(w)
+
+
 @pytest.mark.parametrize("S", [1024, 1025])
 def test_longest_first_order_at_the_sequence_limit(S):
     """1,024 sequences (the most the order kernel ranks) and 1,025 (the given order) x 8 heads
