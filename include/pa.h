@@ -107,7 +107,9 @@ int pa_write_kv(void* k_pool, void* v_pool, int64_t num_blocks,
 /*
  * pa_decode_workspace_bytes — bytes of device workspace pa_decode needs for
  * a batch whose longest context is max_context_len (0 when no sequence is
- * split into more than one context partition).  Host-only, never fails.
+ * split into more than one context partition): the partial results of split
+ * contexts, then room for the order in which a large launch dispatches its
+ * sequences.  Host-only, never fails.
  */
 size_t pa_decode_workspace_bytes(int32_t num_tokens, int32_t num_heads, int32_t head_dim,
                                  int32_t max_context_len);
